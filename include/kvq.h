@@ -1,0 +1,160 @@
+/*
+ * kvq.h - C ABI of libkvq: entropy-coded KV-cache quantisation for AMD MI355X
+ * (gfx950).  Write side: per-token key/value streams are Hadamard-rotated,
+ * keys lose a windowed channel mean, every stream gets one affine grid
+ * (scale, offset), symbols are assigned under a rate budget ("drift") and
+ * rANS-coded into a container of exactly C bytes.  Read side: a fused kernel
+ * decodes the containers at fixed stride and computes softmax(q K^T) V.
+ *
+ * The method is the one of "D-Quant: Driftable Entropy Coding for KV Cache
+ * Quantization" (arXiv 2609.19880), cited below as [D-Quant].
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers owned and allocated by the caller
+ *    (e.g. torch tensors' data_ptr()); all must be 16-byte aligned, else
+ *    KVQ_EINVAL.  Scalars and small out-arrays are host memory.
+ *  - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *    the default stream).  Argument errors return synchronously with nothing
+ *    launched; a failed launch returns KVQ_EDEVICE; faults inside kernels
+ *    surface at the caller's next synchronisation.
+ *  - The library allocates no device memory on the encode/decode path; a
+ *    plan owns only host-side tables.  There is no global error state.
+ *  - Inputs must be finite; NaN/Inf input is undefined behaviour.
+ *  - Layouts are row-major.  A "stream" is one token of one sequence:
+ *    n = n_kv_heads * head_dim values ordered [kv_head][dim].  A "sequence"
+ *    is one (layer, batch) cache; layers fold into the sequence count.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = -1,        /* bad argument, shape or alignment              */
+  KVQ_EINFEASIBLE = -2,   /* container too small for n cheapest symbols    */
+  KVQ_EUNSUPPORTED = -3,  /* valid but not implemented (e.g. head_dim)     */
+  KVQ_EDEVICE = -4,       /* a HIP call or kernel launch failed            */
+  KVQ_ENOMEM = -5,        /* host allocation failed                        */
+  KVQ_EWORKSPACE = -6     /* workspace smaller than kvq_workspace_bytes()  */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+/* Configuration of one cache format ([D-Quant] §4.2, §4.4, §5.1: container
+ * bytes, number of levels and the K/V split are free parameters; the page's
+ * default is 331/231 bytes, 8/6 levels, alpha = 1.4, 2.26 bits per value). */
+typedef struct {
+  int32_t n_kv_heads;         /* Hkv >= 1                                     */
+  int32_t head_dim;           /* d: power of two, 32..256                     */
+  int32_t levels_k;           /* M_K in [2, 16]                               */
+  int32_t levels_v;           /* M_V in [2, 16]                               */
+  int32_t container_bytes_k;  /* C_K > 4 (4 bytes hold the final rANS state)  */
+  int32_t container_bytes_v;  /* C_V > 4                                      */
+  int32_t mean_window;        /* W: power of two; tokens per key-mean window  */
+  double sharpen_alpha;       /* alpha >= 1; probabilities p^alpha ([D-Quant] §4.4) */
+} kvq_params;
+
+/* Immutable plan: the integer rANS tables derived from the Gaussian
+ * order-statistics model ([D-Quant] §4.2), the fixed-point rate tables and
+ * the lambda grid of the drift solver (Appendix A, Algorithm 1).  Pure host
+ * object; safe to share between threads. */
+typedef struct kvq_plan kvq_plan;
+
+/* Builds a plan.  Returns KVQ_EINVAL for out-of-range params,
+ * KVQ_EINFEASIBLE if n * min_m r(m) exceeds 8C - 32 bits for K or V (Eq. 3:
+ * even the cheapest symbol everywhere would not fit), KVQ_ENOMEM. */
+kvq_status kvq_plan_create(const kvq_params* params, kvq_plan** out_plan);
+void kvq_plan_destroy(kvq_plan* plan);
+
+/* Copies one side's tables (side 0 = keys, 1 = values) to host arrays of at
+ * least 16 entries: frequencies f_m (sum 256), cumulative c_m and the rates
+ * r_fx[m] = rne((8 - log2 f_m) * 2^16).  Entries >= levels are zero. */
+kvq_status kvq_plan_tables(const kvq_plan* plan, int side, uint16_t* freq,
+                           uint16_t* cum, int32_t* rate_fx);
+
+/* Copies the 512-entry lambda grid E[k] = fp32(2^(k/512)) to host memory. */
+kvq_status kvq_plan_lambda_grid(const kvq_plan* plan, float* grid512);
+
+/* Storage cost in bits per value ([D-Quant] §3.1: symbols and metadata).
+ * metadata != 0 counts, per token-layer, two fp16 (scale, offset) pairs and
+ * the INT8 key mean of n values plus its fp16 scale per W tokens:
+ * 8 (C_K + C_V + 8 + (n + 2) / W) / (2 n).  metadata == 0: containers only. */
+double kvq_bits_per_elem(const kvq_params* params, int metadata);
+
+/* Container sizes for a budget in bits per value (metadata included):
+ * total = floor(bpe 2n/8 - 8 - (n+2)/W) bytes split 331:562 between K and V
+ * (the page's default split, §5.1), so 2.26 gives 331/231. */
+kvq_status kvq_containers_for_budget(double bits_per_elem, int32_t n_kv_heads,
+                                     int32_t head_dim, int32_t mean_window,
+                                     int32_t* c_k, int32_t* c_v);
+
+/* Device workspace needed by kvq_decode_attention (op = 1) for the given
+ * shape; op = 0 (encode) needs none and reports 0. */
+kvq_status kvq_workspace_bytes(const kvq_plan* plan, int op, int64_t n_seqs,
+                               int64_t seq_len, int32_t n_q_heads, size_t* bytes);
+
+/* Write side ([D-Quant] Figure 1, §4.2-§4.3, Appendix A Algorithm 1).
+ *   k, v          [n_seqs, seq_len, Hkv, d] in `in_dtype` (fp32 or bf16)
+ *   k_cont, v_cont out [n_seqs, seq_len, C_K] / [.., C_V] bytes; every row is
+ *                 exactly C bytes: 4-byte little-endian final state, payload
+ *                 (read forwards by the decoder), zero padding
+ *   k_so, v_so    out [n_seqs, seq_len, 2] fp16 bits: (scale, offset)
+ *   k_mean_q      out [n_seqs, seq_len/W, n] int8 key channel means
+ *   k_mean_scale  out [n_seqs, seq_len/W] fp16 bits
+ *   stats         nullable device uint64[8], ACCUMULATED (caller zeroes it):
+ *                 [0] K streams whose first drift fell back to the cheapest
+ *                 symbol, [1] same for the second drift, [2] K symbols that
+ *                 differ from nearest rounding on the final grid, [3] K
+ *                 streams that overran their container (always 0), [4..7] the
+ *                 same for V.
+ * seq_len must be a positive multiple of W.  Output is deterministic and
+ * independent of launch geometry. */
+kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v,
+                              kvq_dtype in_dtype, int64_t n_seqs, int64_t seq_len,
+                              uint8_t* k_cont, uint8_t* v_cont,
+                              uint16_t* k_so, uint16_t* v_so,
+                              int8_t* k_mean_q, uint16_t* k_mean_scale,
+                              uint64_t* stats, void* hip_stream);
+
+/* Read side ([D-Quant] §4.5 "Decoding", Appendix A Algorithm 2 and
+ * Eqs. (7)-(9)): one decode query per sequence attends over all seq_len
+ * cached tokens; query head h reads KV head h / (Hq / Hkv).
+ *   q             [n_seqs, Hq, d] bf16
+ *   k_cont ...    as written by kvq_encode_streams
+ *   softmax_scale <= 0 selects 1/sqrt(d)
+ *   out           [n_seqs, Hq, d] bf16 (round-to-nearest-even of out_f32)
+ *   out_f32       nullable [n_seqs, Hq, d] fp32
+ *   workspace     device memory of at least kvq_workspace_bytes(plan, 1, ...)
+ * Results are deterministic for a given shape. */
+kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                                const uint8_t* k_cont, const uint8_t* v_cont,
+                                const uint16_t* k_so, const uint16_t* v_so,
+                                const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                                int64_t n_seqs, int64_t seq_len, float softmax_scale,
+                                void* out, float* out_f32,
+                                void* workspace, size_t workspace_bytes,
+                                void* hip_stream);
+
+/* Decodes containers back to symbol indices (Appendix A, Algorithm 2); a
+ * verification helper.  side 0 = K table, 1 = V table.
+ *   cont      [n_streams, C] bytes;  symbols out [n_streams, n] uint8
+ *   end_ok    nullable out [n_streams] uint32: 1 if the final state equals
+ *             2^23 (a well-formed stream ends where the encoder started). */
+kvq_status kvq_decode_symbols(const kvq_plan* plan, int side, const uint8_t* cont,
+                              int64_t n_streams, uint8_t* symbols, uint32_t* end_ok,
+                              void* hip_stream);
+
+/* Static description of a status code. */
+const char* kvq_status_str(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

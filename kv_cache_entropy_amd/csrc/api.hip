@@ -1,0 +1,253 @@
+// C ABI entry points that launch device work (the host-only entry points are
+// in plan.cpp).  Argument checking happens here, before anything is enqueued.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "device_common.h"
+
+namespace kvq {
+bool attention_supported(int Hq, int G, int d);
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Split-K geometry of the decode attention: 64-token tiles; enough splits to
+// give the chip about 2048 workgroups.
+void split_geometry(int64_t S, int64_t T, int* nsplit, int64_t* tokens_per_split) {
+  const int64_t tiles = T / 64;
+  int64_t want = (2048 + S - 1) / S;
+  if (want < 1) want = 1;
+  if (want > tiles) want = tiles;
+  const int64_t tiles_per = (tiles + want - 1) / want;
+  *tokens_per_split = tiles_per * 64;
+  *nsplit = int((tiles + tiles_per - 1) / tiles_per);
+}
+
+struct WsLayout {
+  size_t qrot, qsum, qmu, part, total;
+};
+
+WsLayout ws_layout(const kvq_plan* plan, int64_t S, int64_t T, int Hq) {
+  int nsplit;
+  int64_t tps;
+  split_geometry(S, T, &nsplit, &tps);
+  const int d = plan->params.head_dim;
+  const int64_t nW = T / plan->params.mean_window;
+  WsLayout w;
+  w.qrot = 0;
+  w.qsum = round256(w.qrot + size_t(S) * Hq * d * 4);
+  w.qmu = round256(w.qsum + size_t(S) * Hq * 4);
+  w.part = round256(w.qmu + size_t(S) * Hq * nW * 4);
+  w.total = round256(w.part + size_t(S) * nsplit * Hq * (d + 4) * 4);
+  return w;
+}
+
+kvq::EncTabs enc_tabs(const kvq_plan* plan, int side) {
+  const kvq::SideTables& t = plan->side[side];
+  kvq::EncTabs e;
+  std::memset(&e, 0, sizeof(e));
+  for (int m = 0; m < kvq::kMaxLevels; ++m) {
+    e.rate_fx[m] = t.rate_fx[m];
+    e.freq[m] = t.freq[m];
+    e.cum[m] = t.cum[m];
+    e.rcp[m] = t.rcp[m];
+    e.rshift[m] = t.rshift[m];
+  }
+  std::memcpy(e.lambda, plan->lambda_grid, sizeof(e.lambda));
+  e.levels = t.levels;
+  e.container_bytes = t.container_bytes;
+  e.cheapest = t.cheapest;
+  e.budget_fx = t.budget_fx;
+  return e;
+}
+
+// Streams per encode workgroup: the largest of 32/16/8/4 that divides the
+// stream count and keeps the symbol and container staging under 56 KiB.
+int pick_spw(int64_t n_streams, int n, int C) {
+  for (int spw = 32; spw >= 4; spw >>= 1)
+    if (n_streams % spw == 0 && size_t(spw) * (size_t(n) + size_t(C)) <= 56u * 1024u) return spw;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_workspace_bytes(const kvq_plan* plan, int op, int64_t n_seqs, int64_t seq_len,
+                               int32_t n_q_heads, size_t* bytes) {
+  if (!plan || !bytes || n_seqs < 1 || seq_len < 1) return KVQ_EINVAL;
+  if (op == 0) {
+    *bytes = 0;
+    return KVQ_OK;
+  }
+  if (op != 1 || n_q_heads < 1) return KVQ_EINVAL;
+  *bytes = ws_layout(plan, n_seqs, seq_len, n_q_heads).total;
+  return KVQ_OK;
+}
+
+kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v,
+                              kvq_dtype in_dtype, int64_t n_seqs, int64_t seq_len,
+                              uint8_t* k_cont, uint8_t* v_cont, uint16_t* k_so, uint16_t* v_so,
+                              int8_t* k_mean_q, uint16_t* k_mean_scale, uint64_t* stats,
+                              void* hip_stream) {
+  if (!plan || !k || !v || !k_cont || !v_cont || !k_so || !v_so || !k_mean_q || !k_mean_scale)
+    return KVQ_EINVAL;
+  if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return KVQ_EINVAL;
+  const void* ptrs[] = {k, v, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return KVQ_EINVAL;
+  if (stats && (reinterpret_cast<uintptr_t>(stats) & 7u)) return KVQ_EINVAL;
+  const kvq_params& P = plan->params;
+  const int n = plan->n;
+  const int W = P.mean_window;
+  if (n_seqs < 1 || seq_len < W || seq_len % W) return KVQ_EINVAL;
+  if (n % 64 || n > 4096) return KVQ_EUNSUPPORTED;
+  const int64_t n_streams = n_seqs * seq_len;
+  const int spw_k = pick_spw(n_streams, n, P.container_bytes_k);
+  const int spw_v = pick_spw(n_streams, n, P.container_bytes_v);
+  if (!spw_k || !spw_v) return KVQ_EUNSUPPORTED;
+  if (n_streams / 4 > int64_t(0x7FFFFFFF)) return KVQ_EUNSUPPORTED;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+
+  kvq::KeyMeanArgs km;
+  km.k = k;
+  km.in_bf16 = in_dtype == KVQ_BF16;
+  km.mean_q = k_mean_q;
+  km.mean_scale = k_mean_scale;
+  km.T = seq_len;
+  km.W = W;
+  km.n = n;
+  km.d = P.head_dim;
+  km.hscale = plan->hadamard_scale;
+  if (kvq::launch_key_mean(km, n_seqs * (seq_len / W), stream) != hipSuccess) return KVQ_EDEVICE;
+
+  for (int side = 0; side < 2; ++side) {
+    kvq::EncodeArgs ea;
+    std::memset(&ea, 0, sizeof(ea));
+    ea.x = side == 0 ? k : v;
+    ea.in_bf16 = in_dtype == KVQ_BF16;
+    ea.is_key = side == 0;
+    ea.mean_q = k_mean_q;
+    ea.mean_scale = k_mean_scale;
+    ea.cont = side == 0 ? k_cont : v_cont;
+    ea.so = side == 0 ? k_so : v_so;
+    ea.stats = stats ? reinterpret_cast<unsigned long long*>(stats) + 4 * side : nullptr;
+    ea.T = seq_len;
+    ea.W = W;
+    ea.n = n;
+    ea.d = P.head_dim;
+    ea.hscale = plan->hadamard_scale;
+    ea.spw = side == 0 ? spw_k : spw_v;
+    ea.tabs = enc_tabs(plan, side);
+    if (kvq::launch_encode(ea, n_streams, stream) != hipSuccess) return KVQ_EDEVICE;
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                                const uint8_t* k_cont, const uint8_t* v_cont,
+                                const uint16_t* k_so, const uint16_t* v_so,
+                                const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                                int64_t n_seqs, int64_t seq_len, float softmax_scale,
+                                void* out, float* out_f32, void* workspace,
+                                size_t workspace_bytes, void* hip_stream) {
+  if (!plan || !q || !k_cont || !v_cont || !k_so || !v_so || !k_mean_q || !k_mean_scale || !out ||
+      !workspace)
+    return KVQ_EINVAL;
+  const void* ptrs[] = {q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return KVQ_EINVAL;
+  if (out_f32 && !aligned16(out_f32)) return KVQ_EINVAL;
+  const kvq_params& P = plan->params;
+  const int Hkv = P.n_kv_heads, d = P.head_dim, W = P.mean_window;
+  if (n_q_heads < 1 || n_q_heads % Hkv) return KVQ_EINVAL;
+  if (n_seqs < 1 || seq_len < W || seq_len % W) return KVQ_EINVAL;
+  const int G = n_q_heads / Hkv;
+  if (seq_len % 64 || !kvq::attention_supported(n_q_heads, G, d)) return KVQ_EUNSUPPORTED;
+  if (n_seqs > 65535) return KVQ_EUNSUPPORTED;
+  const WsLayout wl = ws_layout(plan, n_seqs, seq_len, n_q_heads);
+  if (workspace_bytes < wl.total) return KVQ_EWORKSPACE;
+  int nsplit;
+  int64_t tps;
+  split_geometry(n_seqs, seq_len, &nsplit, &tps);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* qrot = reinterpret_cast<float*>(ws + wl.qrot);
+  float* qsum = reinterpret_cast<float*>(ws + wl.qsum);
+  float* qmu = reinterpret_cast<float*>(ws + wl.qmu);
+  float* part = reinterpret_cast<float*>(ws + wl.part);
+
+  kvq::PrologueArgs pa;
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.mean_q = k_mean_q;
+  pa.mean_scale = k_mean_scale;
+  pa.qrot = qrot;
+  pa.qsum = qsum;
+  pa.qmu = qmu;
+  pa.nW = seq_len / W;
+  pa.Hq = n_q_heads;
+  pa.G = G;
+  pa.d = d;
+  pa.n = plan->n;
+  pa.hscale = plan->hadamard_scale;
+  if (kvq::launch_prologue(pa, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
+
+  kvq::AttnArgs aa;
+  aa.k_cont = k_cont;
+  aa.v_cont = v_cont;
+  aa.k_so = k_so;
+  aa.v_so = v_so;
+  aa.qrot = qrot;
+  aa.qsum = qsum;
+  aa.qmu = qmu;
+  aa.part = part;
+  aa.T = seq_len;
+  aa.tokens_per_split = tps;
+  aa.nsplit = nsplit;
+  aa.nW = seq_len / W;
+  aa.W = W;
+  aa.CK = P.container_bytes_k;
+  aa.CV = P.container_bytes_v;
+  aa.tau = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
+  std::memcpy(aa.deck, plan->side[0].dec, sizeof(aa.deck));
+  std::memcpy(aa.decv, plan->side[1].dec, sizeof(aa.decv));
+  if (kvq::launch_attention(aa, n_seqs, n_q_heads, G, d, stream) != hipSuccess) return KVQ_EDEVICE;
+
+  kvq::CombineArgs ca;
+  ca.part = part;
+  ca.out = static_cast<uint16_t*>(out);
+  ca.out_f32 = out_f32;
+  ca.nsplit = nsplit;
+  ca.Hq = n_q_heads;
+  ca.d = d;
+  ca.hscale = plan->hadamard_scale;
+  if (kvq::launch_combine(ca, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_symbols(const kvq_plan* plan, int side, const uint8_t* cont,
+                              int64_t n_streams, uint8_t* symbols, uint32_t* end_ok,
+                              void* hip_stream) {
+  if (!plan || (side != 0 && side != 1) || !cont || !symbols || n_streams < 1) return KVQ_EINVAL;
+  if (!aligned16(cont) || !aligned16(symbols) || (end_ok && !aligned16(end_ok))) return KVQ_EINVAL;
+  kvq::DecSymArgs a;
+  a.cont = cont;
+  a.n_streams = n_streams;
+  a.C = plan->side[side].container_bytes;
+  a.n = plan->n;
+  a.sym = symbols;
+  a.end_ok = end_ok;
+  std::memcpy(a.dec, plan->side[side].dec, sizeof(a.dec));
+  if (kvq::launch_decode_symbols(a, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    return KVQ_EDEVICE;
+  return KVQ_OK;
+}
+
+}  // extern "C"

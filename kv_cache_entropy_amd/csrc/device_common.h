@@ -1,0 +1,222 @@
+// Device-side helpers and the argument blocks passed by value to kernels.
+#ifndef KVQ_DEVICE_COMMON_H_
+#define KVQ_DEVICE_COMMON_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+// ----------------------------------------------------------------- encoder
+struct KeyMeanArgs {
+  const void* k;
+  int in_bf16;
+  int8_t* mean_q;
+  uint16_t* mean_scale;
+  int64_t T;
+  int W, n, d;
+  float hscale;
+};
+
+struct EncTabs {
+  uint32_t rate_fx[kMaxLevels];
+  uint32_t freq[kMaxLevels];
+  uint32_t cum[kMaxLevels];
+  uint32_t rcp[kMaxLevels];
+  uint32_t rshift[kMaxLevels];
+  float lambda[kLambdaGrid];
+  int levels;
+  int container_bytes;
+  uint32_t cheapest;
+  uint64_t budget_fx;
+};
+
+struct EncodeArgs {
+  const void* x;
+  int in_bf16;
+  int is_key;
+  const int8_t* mean_q;
+  const uint16_t* mean_scale;
+  uint8_t* cont;
+  uint16_t* so;
+  unsigned long long* stats;   // already offset to the side's 4 counters
+  int64_t T;
+  int W, n, d;
+  float hscale;
+  int spw;                     // streams per workgroup (multiple of 4)
+  EncTabs tabs;
+};
+
+struct EncShared {
+  float lambda[kLambdaGrid];
+  uint32_t rate_fx[kMaxLevels];
+  float rate_f[kMaxLevels];
+  uint32_t freq[kMaxLevels];
+  uint32_t cum[kMaxLevels];
+  uint32_t rcp[kMaxLevels];
+  uint32_t rshift[kMaxLevels];
+  uint32_t cheapest;
+  uint64_t budget_fx;
+};
+
+// ----------------------------------------------------------------- decoder
+struct DecSymArgs {
+  const uint8_t* cont;
+  int64_t n_streams;
+  int C, n;
+  uint8_t* sym;
+  uint32_t* end_ok;
+  uint32_t dec[256];
+};
+
+struct PrologueArgs {
+  const uint16_t* q;          // bf16 [S, Hq, d]
+  const int8_t* mean_q;       // [S, nW, n]
+  const uint16_t* mean_scale; // [S, nW]
+  float* qrot;                // [S, Hq, d]
+  float* qsum;                // [S, Hq]
+  float* qmu;                 // [S, Hq, nW]
+  int64_t nW;
+  int Hq, G, d, n;
+  float hscale;
+};
+
+struct AttnArgs {
+  const uint8_t* k_cont;
+  const uint8_t* v_cont;
+  const uint16_t* k_so;
+  const uint16_t* v_so;
+  const float* qrot;
+  const float* qsum;
+  const float* qmu;
+  float* part;                // [S, nsplit, Hq, d + 4]
+  int64_t T;
+  int64_t tokens_per_split;
+  int nsplit;
+  int64_t nW;
+  int W, CK, CV;
+  float tau;
+  uint32_t deck[256];
+  uint32_t decv[256];
+};
+
+struct CombineArgs {
+  const float* part;
+  uint16_t* out;              // bf16 [S, Hq, d]
+  float* out_f32;             // nullable
+  int nsplit, Hq, d;
+  float hscale;
+};
+
+// ----------------------------------------------------------------- helpers
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ inline float wave_min(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ inline float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ inline int wave_sum_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Loads NPL consecutive values (fp32 or bf16) starting at element `off`.
+template <int NPL>
+__device__ inline void load_values(const void* base, int in_bf16, int64_t off, float (&v)[NPL]) {
+  if (in_bf16) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
+    if constexpr (NPL % 8 == 0) {
+#pragma unroll
+      for (int c = 0; c < NPL / 8; ++c) {
+        const uint4 w = reinterpret_cast<const uint4*>(p)[c];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[c * 8 + 2 * k] = __uint_as_float(ws[k] << 16);
+          v[c * 8 + 2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) v[i] = bf16_bits_to_f32(p[i]);
+    }
+  } else {
+    const float* p = static_cast<const float*>(base) + off;
+    if constexpr (NPL % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < NPL / 4; ++c) {
+        const float4 w = reinterpret_cast<const float4*>(p)[c];
+        v[4 * c] = w.x;
+        v[4 * c + 1] = w.y;
+        v[4 * c + 2] = w.z;
+        v[4 * c + 3] = w.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) v[i] = p[i];
+    }
+  }
+}
+
+// Per-head orthonormal Sylvester Hadamard on values distributed NPL per lane
+// (lane holds global indices lane*NPL .. lane*NPL+NPL-1).  Stage h pairs i and
+// i + h (bit h of i clear) into (a + b, a - b); then everything is scaled by
+// fp32(1/sqrt(d)).
+template <int NPL>
+__device__ inline void fwht_lanes(float (&v)[NPL], int d, int lane, float scale) {
+#pragma unroll
+  for (int h = 1; h < NPL; h <<= 1) {
+    if (h < d) {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        if (!(i & h)) {
+          const float a = v[i], b = v[i + h];
+          v[i] = __fadd_rn(a, b);
+          v[i + h] = __fsub_rn(a, b);
+        }
+      }
+    }
+  }
+  for (int h = NPL; h < d; h <<= 1) {
+    const int lx = h / NPL;
+    const bool upper = (lane & lx) != 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const float p = __shfl_xor(v[i], lx, 64);
+      v[i] = upper ? __fsub_rn(p, v[i]) : __fadd_rn(v[i], p);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) v[i] = __fmul_rn(v[i], scale);
+}
+
+
+hipError_t launch_key_mean(const KeyMeanArgs& a, int64_t n_windows, hipStream_t stream);
+hipError_t launch_encode(const EncodeArgs& a, int64_t n_streams, hipStream_t stream);
+hipError_t launch_decode_symbols(const DecSymArgs& a, hipStream_t stream);
+hipError_t launch_prologue(const PrologueArgs& a, int64_t S, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs& a, int64_t S, int Hq, int G, int d, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream);
+
+}  // namespace kvq
+
+#endif  // KVQ_DEVICE_COMMON_H_

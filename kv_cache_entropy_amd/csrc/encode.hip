@@ -1,0 +1,358 @@
+// Write side: windowed key channel mean and the per-stream encoder.
+//
+// [D-Quant] Figure 1 / §4.2: every head of a token's key (value) vector is
+// Hadamard-rotated; keys subtract a windowed channel-wise mean; each stream
+// (all KV heads of one token) gets one affine grid (Eq. 4).  §4.3 / Appendix
+// A, Algorithm 1: symbols are assigned by a Lagrangian drift under the
+// container budget (Eqs. 5-6), (s, o) are refitted by least squares, rounded
+// to FP16 and the drift repeated on that grid; the symbols are rANS-coded
+// (Eq. 2) backwards into a C-byte container (Eq. 3).  §4.5 "Encoding": one
+// wavefront per stream keeps the values on chip throughout; distortions are
+// recomputed on the fly for the M levels at every bisection step and the code
+// length is reduced across the wavefront.
+//
+// Every floating-point step is one IEEE operation rounded to nearest-even
+// (explicit __f*_rn / __d*_rn intrinsics, no contraction) and every float
+// reduction has a fixed order, so containers are bit-identical to a plain CPU
+// evaluation of the same steps.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "device_common.h"
+
+namespace kvq {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Windowed key channel mean: one workgroup per (sequence, window); thread t
+// owns channels 4t..4t+3.  mu = (fp32 running sum over the window's tokens in
+// order, from +0) * (1/W); INT8 with one fp16 scale: sc = fp16(max|mu| / 127),
+// mu_q = clamp(rne(mu / sc), -127, 127).
+__global__ __launch_bounds__(1024) void key_mean_kernel(KeyMeanArgs a) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t nW = a.T / a.W;
+  const int64_t seq = blockIdx.x / nW;
+  const int64_t win = blockIdx.x % nW;
+  const int j0 = tid * 4;
+  const bool active = j0 < a.n;   // the block is rounded up to whole waves
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < a.W; ++tt) {
+    const int64_t row = (seq * a.T + win * a.W + tt) * a.n;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (active) load_values<4>(a.k, a.in_bf16, row + j0, v);
+    fwht_lanes<4>(v, a.d, lane, a.hscale);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __fadd_rn(acc[i], v[i]);
+  }
+  const float invW = 1.0f / float(a.W);   // exact: W is a power of two
+  float mu[4];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mu[i] = __fmul_rn(acc[i], invW);
+    amax = fmaxf(amax, fabsf(mu[i]));
+  }
+  __shared__ float red[16];
+  amax = wave_max(amax);
+  if (lane == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  const int nwaves = (blockDim.x + 63) >> 6;
+  amax = red[0];
+  for (int w = 1; w < nwaves; ++w) amax = fmaxf(amax, red[w]);
+  const __half sc16 = __float2half_rn(__fdiv_rn(amax, 127.0f));
+  const float sc = __half2float(sc16);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int qv = 0;
+    if (sc != 0.f) {
+      float r = rintf(__fdiv_rn(mu[i], sc));
+      r = fminf(fmaxf(r, -127.f), 127.f);
+      qv = int(r);
+    }
+    packed |= (uint32_t(qv) & 0xFFu) << (8 * i);
+  }
+  const int64_t orow = (seq * nW + win);
+  if (active) *reinterpret_cast<uint32_t*>(a.mean_q + orow * a.n + j0) = packed;
+  if (tid == 0) a.mean_scale[orow] = __half_as_ushort(sc16);
+}
+
+// ---------------------------------------------------------------------------
+// Drift (Algorithm 1) for the stream held NPL values per lane by one wave.
+// Returns true if the encoder fell back to the cheapest symbol everywhere.
+// If near != nullptr, the nearest-level (lambda -> 0) assignment is returned.
+template <int NPL>
+__device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& sh,
+                      int levels, uint8_t (&m)[NPL], uint8_t (*near)[NPL]) {
+  // range of the distortion over all (i, level) and the nearest levels
+  float dmax = 0.f, dmin = __builtin_inff();
+  float bestD[NPL];
+  uint8_t bl[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) { bestD[i] = __builtin_inff(); bl[i] = 0; }
+  for (int l = 0; l < levels; ++l) {
+    const float rec = __fadd_rn(o, __fmul_rn(s, float(l)));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const float dl = __fsub_rn(x[i], rec);
+      const float D = __fmul_rn(dl, dl);
+      dmax = fmaxf(dmax, D);
+      dmin = fminf(dmin, D);
+      if (D < bestD[i]) { bestD[i] = D; bl[i] = uint8_t(l); }
+    }
+  }
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) (*near)[i] = bl[i];
+  }
+  dmax = wave_max(dmax);
+  dmin = wave_min(dmin);
+  const float y = __fmul_rn(__fsub_rn(dmax, dmin), 8.0f);
+  const uint8_t cheap = uint8_t(sh.cheapest);
+  if (!(y > 0.f)) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) m[i] = cheap;
+    return false;
+  }
+  int e;
+  const float fr = frexpf(y, &e);
+  const int hi0 = (fr == 0.5f) ? e - 1 : e;
+  int lo = 512 * (hi0 - 40), hi = 512 * hi0;
+  bool moved = false;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) m[i] = cheap;
+  uint8_t cur[NPL];
+  for (int step = 0; step <= 12; ++step) {
+    int u;
+    if (step < 12) {
+      u = (lo + hi) >> 1;              // lo + hi is always even: exact
+    } else {
+      if (moved) break;
+      u = hi;                          // never feasible inside: try 2^hi
+    }
+    const float lam = ldexpf(sh.lambda[u & 511], u >> 9);
+    float best[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) { best[i] = __builtin_inff(); cur[i] = 0; }
+    for (int l = 0; l < levels; ++l) {
+      const float rec = __fadd_rn(o, __fmul_rn(s, float(l)));
+      const float lr = __fmul_rn(lam, sh.rate_f[l]);
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const float dl = __fsub_rn(x[i], rec);
+        const float obj = __fadd_rn(__fmul_rn(dl, dl), lr);
+        if (obj < best[i]) { best[i] = obj; cur[i] = uint8_t(l); }
+      }
+    }
+    uint32_t R = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) R += sh.rate_fx[cur[i]];
+    R = wave_sum_u32(R);
+    const bool ok = uint64_t(R) <= sh.budget_fx;
+    if (step < 12) {
+      if (ok) {
+        hi = u;
+        moved = true;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) m[i] = cur[i];
+      } else {
+        lo = u;
+      }
+    } else {
+      if (!ok) return true;            // fallback: cheapest level everywhere
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) m[i] = cur[i];
+    }
+  }
+  return false;
+}
+
+// Least-squares refit in float64 with the fixed summation order (chunk per
+// lane in increasing index from +0, then xor-butterfly 32..1), the guard, and
+// rounding to fp16 through fp32.
+template <int NPL>
+__device__ void refit(const float (&x)[NPL], const uint8_t (&m)[NPL], float s, float o, int n,
+                      __half& s16, __half& o16) {
+  double px = 0.0, pmx = 0.0;
+  int s1 = 0, s2 = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const double xd = double(x[i]);
+    px = __dadd_rn(px, xd);
+    pmx = __dadd_rn(pmx, __dmul_rn(double(m[i]), xd));
+    s1 += m[i];
+    s2 += int(m[i]) * int(m[i]);
+  }
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) {
+    px = __dadd_rn(px, __shfl_xor(px, k, 64));
+    pmx = __dadd_rn(pmx, __shfl_xor(pmx, k, 64));
+  }
+  const int64_t S1 = wave_sum_i32(s1);
+  const int64_t S2 = wave_sum_i32(s2);
+  const int64_t den = int64_t(n) * S2 - S1 * S1;
+  const double S1d = double(S1), nd = double(n);
+  double sn, on;
+  if (den == 0) {
+    sn = double(s);
+    on = __ddiv_rn(__dsub_rn(px, __dmul_rn(sn, S1d)), nd);
+  } else {
+    sn = __ddiv_rn(__dsub_rn(__dmul_rn(nd, pmx), __dmul_rn(S1d, px)), double(den));
+    on = __ddiv_rn(__dsub_rn(px, __dmul_rn(sn, S1d)), nd);
+  }
+  if (!(sn >= 0.0) || !isfinite(sn) || !isfinite(on)) {
+    sn = double(s);
+    on = double(o);
+  }
+  s16 = __float2half_rn(float(sn));
+  o16 = __float2half_rn(float(on));
+}
+
+// rANS encoder of one stream (one lane): symbols sym[0..n), from the last to
+// the first; pushed bytes are written downwards from img[C-1], then moved to
+// follow the 4-byte state.  Returns false if the stream would overrun.
+__device__ bool rans_encode_lane(const uint8_t* sym, int n, uint8_t* img, int C, const EncShared& sh) {
+  uint32_t x = kStateLow;
+  int k = 0;
+  bool ok = true;
+  for (int i = n - 1; i >= 0; --i) {
+    const int mm = sym[i];
+    const uint32_t f = sh.freq[mm];
+    if (x >= (f << 23)) {
+      if (k < C - 4) {
+        img[C - 1 - k] = uint8_t(x & 0xFF);
+        ++k;
+      } else {
+        ok = false;
+      }
+      x >>= 8;
+    }
+    const uint32_t rcp = sh.rcp[mm];
+    const uint32_t q = rcp ? (__umulhi(x, rcp) >> sh.rshift[mm]) : (x >> sh.rshift[mm]);
+    x = (q << 8) + (x - q * f) + sh.cum[mm];
+  }
+  img[0] = uint8_t(x);
+  img[1] = uint8_t(x >> 8);
+  img[2] = uint8_t(x >> 16);
+  img[3] = uint8_t(x >> 24);
+  for (int j = 0; j < k; ++j) img[4 + j] = img[C - k + j];
+  for (int j = 4 + k; j < C; ++j) img[j] = 0;
+  return ok;
+}
+
+// One workgroup = 4 waves = SPW streams of one side.  Each wave runs
+// Algorithm 1 on SPW/4 streams in turn (values stay in registers); then SPW
+// lanes rANS-code the streams from LDS and the workgroup copies the SPW
+// contiguous containers out with dword stores.
+template <int NPL>
+__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  __shared__ EncShared sh;
+  __shared__ uint32_t so_sh[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int SPW = a.spw;
+  const int n = a.n, C = a.tabs.container_bytes, M = a.tabs.levels;
+  uint8_t* sym = dyn;                      // [SPW][n]
+  uint8_t* img = dyn + size_t(SPW) * n;    // [SPW][C]
+  for (int i = tid; i < 512; i += 256) sh.lambda[i] = a.tabs.lambda[i];
+  if (tid < kMaxLevels) {
+    sh.rate_fx[tid] = a.tabs.rate_fx[tid];
+    sh.rate_f[tid] = float(a.tabs.rate_fx[tid]) * (1.0f / 65536.0f);
+    sh.freq[tid] = a.tabs.freq[tid];
+    sh.cum[tid] = a.tabs.cum[tid];
+    sh.rcp[tid] = a.tabs.rcp[tid];
+    sh.rshift[tid] = a.tabs.rshift[tid];
+  }
+  if (tid == 0) {
+    sh.cheapest = a.tabs.cheapest;
+    sh.budget_fx = a.tabs.budget_fx;
+  }
+  __syncthreads();
+  const int64_t stream0 = int64_t(blockIdx.x) * SPW;
+  const int per_wave = SPW / 4;
+  uint32_t fb1 = 0, fb2 = 0, changed = 0;
+  for (int js = 0; js < per_wave; ++js) {
+    const int sl = wave * per_wave + js;
+    const int64_t st = stream0 + sl;
+    float x[NPL];
+    load_values<NPL>(a.x, a.in_bf16, st * n + int64_t(lane) * NPL, x);
+    fwht_lanes<NPL>(x, a.d, lane, a.hscale);
+    if (a.is_key) {
+      const int64_t seq = st / a.T, t = st % a.T;
+      const int64_t row = seq * (a.T / a.W) + t / a.W;
+      const float sc = __half2float(__ushort_as_half(a.mean_scale[row]));
+      const int8_t* mq = a.mean_q + row * n + int64_t(lane) * NPL;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) x[i] = __fsub_rn(x[i], __fmul_rn(float(mq[i]), sc));
+    }
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+    mn = __fadd_rn(wave_min(mn), 0.0f);     // a negative zero becomes +0
+    mx = __fadd_rn(wave_max(mx), 0.0f);
+    const float s = __fdiv_rn(__fsub_rn(mx, mn), float(M - 1));
+    const float o = mn;
+    uint8_t m[NPL];
+    fb1 += drift<NPL>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
+    __half s16, o16;
+    refit<NPL>(x, m, s, o, n, s16, o16);
+    uint8_t nearest[NPL];
+    fb2 += drift<NPL>(x, __half2float(s16), __half2float(o16), sh, M, m, &nearest) ? 1u : 0u;
+    uint32_t ch = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) ch += (m[i] != nearest[i]) ? 1u : 0u;
+    changed += wave_sum_u32(ch);
+    uint8_t* dst = sym + size_t(sl) * n + size_t(lane) * NPL;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) dst[i] = m[i];
+    if (lane == 0) so_sh[sl] = uint32_t(__half_as_ushort(s16)) | (uint32_t(__half_as_ushort(o16)) << 16);
+  }
+  __syncthreads();
+  uint32_t overrun = 0;
+  if (tid < SPW) {
+    overrun = rans_encode_lane(sym + size_t(tid) * n, n, img + size_t(tid) * C, C, sh) ? 0u : 1u;
+    reinterpret_cast<uint32_t*>(a.so)[stream0 + tid] = so_sh[tid];
+  }
+  __syncthreads();
+  // SPW * C is a multiple of 4 (SPW is a multiple of 4); the base is 16-aligned
+  const int nwords = SPW * C / 4;
+  uint32_t* gdst = reinterpret_cast<uint32_t*>(a.cont + stream0 * C);
+  const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(img);
+  for (int i = tid; i < nwords; i += 256) gdst[i] = ssrc[i];
+  if (a.stats) {
+    if (lane == 0) {
+      if (fb1) atomicAdd(a.stats + 0, (unsigned long long)fb1);
+      if (fb2) atomicAdd(a.stats + 1, (unsigned long long)fb2);
+      if (changed) atomicAdd(a.stats + 2, (unsigned long long)changed);
+    }
+    if (overrun) atomicAdd(a.stats + 3, 1ull);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_key_mean(const KeyMeanArgs& a, int64_t n_windows, hipStream_t stream) {
+  const int threads = ((a.n / 4 + 63) / 64) * 64;
+  hipLaunchKernelGGL(key_mean_kernel, dim3(unsigned(n_windows)), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs& a, int64_t n_streams, hipStream_t stream) {
+  const size_t lds = size_t(a.spw) * (size_t(a.n) + size_t(a.tabs.container_bytes));
+  const dim3 grid(unsigned(n_streams / a.spw)), block(256);
+  switch (a.n / 64) {
+    case 1: hipLaunchKernelGGL(encode_kernel<1>, grid, block, lds, stream, a); break;
+    case 2: hipLaunchKernelGGL(encode_kernel<2>, grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL(encode_kernel<4>, grid, block, lds, stream, a); break;
+    case 8: hipLaunchKernelGGL(encode_kernel<8>, grid, block, lds, stream, a); break;
+    case 16: hipLaunchKernelGGL(encode_kernel<16>, grid, block, lds, stream, a); break;
+    case 32: hipLaunchKernelGGL(encode_kernel<32>, grid, block, lds, stream, a); break;
+    case 64: hipLaunchKernelGGL(encode_kernel<64>, grid, block, lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

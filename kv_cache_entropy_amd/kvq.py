@@ -1,0 +1,191 @@
+"""Thin Python binding of libkvq (include/kvq.h): argument marshalling only.
+
+Every function below has the name of the C entry point it calls.  Tensors are
+torch tensors on the GPU; their data pointers and the current HIP stream are
+passed straight through.  Every step of the computation runs in the HIP
+library; if it is not built this module raises instead of doing anything else.
+"""
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime libkvq links against (same soname)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_F32, KVQ_BF16 = 0, 1
+_STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_EINFEASIBLE", -3: "KVQ_EUNSUPPORTED",
+           -4: "KVQ_EDEVICE", -5: "KVQ_ENOMEM", -6: "KVQ_EWORKSPACE"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = lib().kvq_status_str(status).decode()
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} ({msg})")
+
+
+class kvq_params(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("levels_k", ctypes.c_int32), ("levels_v", ctypes.c_int32),
+                ("container_bytes_k", ctypes.c_int32), ("container_bytes_v", ctypes.c_int32),
+                ("mean_window", ctypes.c_int32), ("sharpen_alpha", ctypes.c_double)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _U64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+_SIGS = {
+    "kvq_plan_create": (_I32, [ctypes.POINTER(kvq_params), ctypes.POINTER(_P)]),
+    "kvq_plan_destroy": (None, [_P]),
+    "kvq_plan_tables": (_I32, [_P, ctypes.c_int, _P, _P, _P]),
+    "kvq_plan_lambda_grid": (_I32, [_P, _P]),
+    "kvq_bits_per_elem": (ctypes.c_double, [ctypes.POINTER(kvq_params), ctypes.c_int]),
+    "kvq_containers_for_budget": (_I32, [ctypes.c_double, _I32, _I32, _I32,
+                                         ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "kvq_workspace_bytes": (_I32, [_P, ctypes.c_int, _I64, _I64, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "kvq_encode_streams": (_I32, [_P, _P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kvq_decode_attention": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float,
+                                    _P, _P, _P, ctypes.c_size_t, _P]),
+    "kvq_decode_symbols": (_I32, [_P, ctypes.c_int, _P, _I64, _P, _P, _P]),
+    "kvq_status_str": (ctypes.c_char_p, [_I32]),
+}
+
+
+def lib():
+    """Loads libkvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_entropy_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise KvqError(fn, status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """Owns a kvq_plan (host-side tables of one cache format)."""
+
+    def __init__(self, n_kv_heads, head_dim, levels_k=8, levels_v=6, container_bytes_k=331,
+                 container_bytes_v=231, mean_window=128, sharpen_alpha=1.4):
+        self.params = kvq_params(n_kv_heads, head_dim, levels_k, levels_v, container_bytes_k,
+                                 container_bytes_v, mean_window, sharpen_alpha)
+        h = ctypes.c_void_p()
+        _check("kvq_plan_create", lib().kvq_plan_create(ctypes.byref(self.params), ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.kvq_plan_destroy(h)
+            self.handle = None
+
+    @property
+    def n(self):
+        return self.params.n_kv_heads * self.params.head_dim
+
+    def tables(self, side):
+        """(freq, cum, rate_fx) lists of length `levels` for side 0 (K) / 1 (V)."""
+        f = (ctypes.c_uint16 * 16)()
+        c = (ctypes.c_uint16 * 16)()
+        r = (ctypes.c_int32 * 16)()
+        _check("kvq_plan_tables", lib().kvq_plan_tables(self.handle, side, f, c, r))
+        M = self.params.levels_k if side == 0 else self.params.levels_v
+        return list(f)[:M], list(c)[:M], list(r)[:M]
+
+    def lambda_grid(self):
+        g = (ctypes.c_float * 512)()
+        _check("kvq_plan_lambda_grid", lib().kvq_plan_lambda_grid(self.handle, g))
+        return list(g)
+
+    def bits_per_elem(self, metadata=True):
+        return lib().kvq_bits_per_elem(ctypes.byref(self.params), int(bool(metadata)))
+
+    def workspace_bytes(self, op, n_seqs, seq_len, n_q_heads):
+        b = ctypes.c_size_t()
+        _check("kvq_workspace_bytes", lib().kvq_workspace_bytes(
+            self.handle, op, n_seqs, seq_len, n_q_heads, ctypes.byref(b)))
+        return b.value
+
+
+def kvq_containers_for_budget(bits_per_elem, n_kv_heads, head_dim, mean_window):
+    ck, cv = _I32(), _I32()
+    _check("kvq_containers_for_budget", lib().kvq_containers_for_budget(
+        bits_per_elem, n_kv_heads, head_dim, mean_window, ctypes.byref(ck), ctypes.byref(cv)))
+    return ck.value, cv.value
+
+
+def kvq_encode_streams(plan, k, v, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale,
+                       stats=None, stream=None):
+    """k, v: [S, T, Hkv, d] (or [S, T, n]) fp32/bf16 CUDA tensors; outputs as in kvq.h."""
+    if k.dtype != v.dtype or k.shape != v.shape:
+        raise ValueError("k and v must have the same dtype and shape")
+    dt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}.get(k.dtype)
+    if dt is None:
+        raise TypeError("k/v must be float32 or bfloat16")
+    S, T = int(k.shape[0]), int(k.shape[1])
+    _check("kvq_encode_streams", lib().kvq_encode_streams(
+        plan.handle, _ptr(k), _ptr(v), dt, S, T, _ptr(k_cont), _ptr(v_cont), _ptr(k_so),
+        _ptr(v_so), _ptr(k_mean_q), _ptr(k_mean_scale), _ptr(stats), _stream(stream)))
+
+
+def kvq_decode_attention(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, out,
+                         workspace, out_f32=None, softmax_scale=0.0, stream=None):
+    """q: [S, Hq, d] bf16; out: [S, Hq, d] bf16; workspace: uint8 CUDA tensor."""
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("q and out must be bfloat16")
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    T = int(k_cont.shape[1])
+    _check("kvq_decode_attention", lib().kvq_decode_attention(
+        plan.handle, _ptr(q), Hq, _ptr(k_cont), _ptr(v_cont), _ptr(k_so), _ptr(v_so),
+        _ptr(k_mean_q), _ptr(k_mean_scale), S, T, float(softmax_scale), _ptr(out), _ptr(out_f32),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def kvq_decode_symbols(plan, side, cont, symbols, end_ok=None, stream=None):
+    """cont: [..., C] uint8; symbols: [..., n] uint8; end_ok: nullable int32/uint32-sized."""
+    n_streams = cont.numel() // cont.shape[-1]
+    _check("kvq_decode_symbols", lib().kvq_decode_symbols(
+        plan.handle, side, _ptr(cont), n_streams, _ptr(symbols), _ptr(end_ok), _stream(stream)))
+
+
+def alloc_cache(plan, n_seqs, seq_len, device="cuda"):
+    """Empty output tensors for kvq_encode_streams (plumbing only)."""
+    p = plan.params
+    nW = seq_len // p.mean_window
+    e = lambda *shape, dtype: torch.empty(*shape, dtype=dtype, device=device)
+    return {
+        "k_cont": e(n_seqs, seq_len, p.container_bytes_k, dtype=torch.uint8),
+        "v_cont": e(n_seqs, seq_len, p.container_bytes_v, dtype=torch.uint8),
+        "k_so": e(n_seqs, seq_len, 2, dtype=torch.int16),
+        "v_so": e(n_seqs, seq_len, 2, dtype=torch.int16),
+        "k_mean_q": e(n_seqs, nW, plan.n, dtype=torch.int8),
+        "k_mean_scale": e(n_seqs, nW, dtype=torch.int16),
+    }

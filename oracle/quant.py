@@ -48,10 +48,13 @@ GRID = 512            # lambda grid points per octave
 
 
 def fit_minmax(x, levels):
-    """Eq. (4): s = (max - min) / (M - 1), o = min (float32, per row)."""
+    """Eq. (4): s = (max - min) / (M - 1), o = min (float32, per row).
+
+    A zero extreme is taken as +0 (min + 0 in round-to-nearest), so the sign
+    of a zero offset never depends on how a -0/+0 tie is resolved."""
     x = np.asarray(x, F32)
-    mn = x.min(axis=1)
-    mx = x.max(axis=1)
+    mn = x.min(axis=1) + F32(0.0)
+    mx = x.max(axis=1) + F32(0.0)
     s = (mx - mn) / F32(levels - 1)
     return s.astype(F32), mn.astype(F32)
 

@@ -1,0 +1,143 @@
+"""GPU parity of the HIP path against the oracle on the same seeded inputs.
+
+Containers, (scale, offset) metadata, INT8 key means, decoded symbols and the
+drift counters must be bit-identical; decode attention must be within 2e-3 of
+the float64 reference row-normwise on the fp32 output, and the bf16 output
+must be the round-to-nearest-even of the fp32 one.  The oracle encodes the
+inputs itself: nothing the GPU produced is ever fed to it."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from kv_cache_entropy_amd import synth
+from tests.oracle_pool import encode_cache_parallel
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _kvq():
+    from kv_cache_entropy_amd import kvq
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return kvq
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu_encode(kvq, plan, k, v):
+    S, T = int(k.shape[0]), int(k.shape[1])
+    c = kvq.alloc_cache(plan, S, T)
+    stats = torch.zeros(8, dtype=torch.int64, device="cuda")
+    kvq.kvq_encode_streams(plan, k, v, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
+                           c["k_mean_q"], c["k_mean_scale"], stats=stats)
+    torch.cuda.synchronize()
+    return c, stats
+
+
+def gpu_attention(kvq, plan, q, c, Hq):
+    S, T = int(c["k_cont"].shape[0]), int(c["k_cont"].shape[1])
+    ws = torch.empty(plan.workspace_bytes(1, S, T, Hq), dtype=torch.uint8, device="cuda")
+    out = torch.empty(S, Hq, plan.params.head_dim, dtype=torch.bfloat16, device="cuda")
+    out32 = torch.empty(S, Hq, plan.params.head_dim, dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_attention(plan, q, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
+                             c["k_mean_q"], c["k_mean_scale"], out, ws, out_f32=out32)
+    torch.cuda.synchronize()
+    return out, out32
+
+
+def oracle_attention(q, r, p):
+    mu_tok = np.repeat(r["mu_hat"], p.mean_window, axis=0)
+    return O.attention_factored_f64(q.astype(np.float64), r["k_sym"], r["k_so"], mu_tok,
+                                    r["v_sym"], r["v_so"], p.n_kv_heads, p.head_dim)
+
+
+def check_attention(out, out32, ref):
+    o32 = out32.cpu().numpy().astype(np.float64)
+    err = (np.abs(o32 - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max()
+    assert err <= TOL, f"attention row-normwise error {err:.3e} > {TOL}"
+    rne = out32.cpu().to(torch.bfloat16).view(torch.int16)
+    assert torch.equal(rne, out.cpu().view(torch.int16))
+    return err
+
+
+def compare_cache(c, stats, refs, p, S):
+    """refs: per-sequence oracle results; c: GPU cache tensors."""
+    for s in range(S):
+        r = refs[s]
+        for key in ("k_cont", "v_cont", "k_mean_q"):
+            got = c[key][s].cpu().numpy().view(np.uint8 if key != "k_mean_q" else np.int8)
+            assert np.array_equal(got, r[key]), f"{key} differs in sequence {s}"
+        for key in ("k_so", "v_so"):
+            got = c[key][s].cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, r[key].view(np.uint16)), f"{key} differs in sequence {s}"
+        got = c["k_mean_scale"][s].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, r["k_mean_scale"].view(np.uint16))
+    tot = np.sum([refs[s]["stats"] for s in range(S)], axis=0)
+    assert stats.cpu().numpy().astype(np.uint64).tolist() == tot.tolist()
+
+
+def run_case(name, budget_idx, seqs, tokens):
+    kvq = _kvq()
+    w = synth.WORKLOADS[name]
+    ck, cv = w.containers[budget_idx]
+    say(f"case {name} budget={w.budgets[budget_idx]} C=({ck},{cv}) seqs={seqs} tokens={tokens}")
+    plan = kvq.Plan(w.n_kv_heads, w.head_dim, 8, 6, ck, cv, 128, 1.4)
+    p = O.OracleParams(w.n_kv_heads, w.head_dim, 8, 6, ck, cv, 128, 1.4)
+    k, v = synth.cache_inputs(w, "cuda", seqs, tokens)
+    q = synth.queries(w, "cuda", seqs)
+    c, stats = gpu_encode(kvq, plan, k, v)
+    say("  gpu encode done")
+    refs = [encode_cache_parallel(k[s].float().cpu().numpy(), v[s].float().cpu().numpy(), p)
+            for s in range(len(seqs))]
+    say("  oracle encode done")
+    compare_cache(c, stats, refs, p, len(seqs))
+    # decoded symbols
+    for side, key, sk in ((0, "k_cont", "k_sym"), (1, "v_cont", "v_sym")):
+        sym = torch.empty(*c[key].shape[:2], p.n, dtype=torch.uint8, device="cuda")
+        ok = torch.zeros(*c[key].shape[:2], dtype=torch.int32, device="cuda")
+        kvq.kvq_decode_symbols(plan, side, c[key], sym, ok)
+        torch.cuda.synchronize()
+        assert int(ok.sum()) == ok.numel()
+        for s in range(len(seqs)):
+            assert np.array_equal(sym[s].cpu().numpy(), refs[s][sk])
+    out, out32 = gpu_attention(kvq, plan, q, c, w.n_q_heads)
+    ref = np.stack([oracle_attention(q[s].float().cpu().numpy(), refs[s], p) for s in range(len(seqs))])
+    err = check_attention(out, out32, ref)
+    say(f"  attention max row-normwise error {err:.3e}")
+
+
+def test_tiny_full():
+    run_case("tiny", 0, [0], None)
+
+
+@pytest.mark.parametrize("name,bi,seqs,tokens", [
+    ("gqa", 0, [0, 511], (0, 512)),
+    ("long", 0, [0, 127], (0, 512)),
+    ("long", 1, [0], (1024, 1536)),
+    ("long", 2, [5], (0, 512)),
+    ("verylong", 0, [0], (0, 1024)),
+    ("heavy", 0, [0, 7], (0, 512)),
+    ("heavy", 1, [3], (0, 512)),
+    ("heavy", 2, [6], (512, 1024)),
+])
+def test_reduced_configs(name, bi, seqs, tokens):
+    run_case(name, bi, seqs, tokens)
+
+
+def test_encode_is_deterministic():
+    kvq = _kvq()
+    w = synth.WORKLOADS["heavy"]
+    plan = kvq.Plan(8, 128, 8, 6, 292, 203, 128, 1.4)
+    k, v = synth.cache_inputs(w, "cuda", [1], (0, 1024))
+    a, sa = gpu_encode(kvq, plan, k, v)
+    b, sb = gpu_encode(kvq, plan, k, v)
+    for key in a:
+        assert torch.equal(a[key], b[key])
+    assert torch.equal(sa, sb)
