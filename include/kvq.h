@@ -150,6 +150,16 @@ kvq_status kvq_decode_symbols(const kvq_plan* plan, int side, const uint8_t* con
                               int64_t n_streams, uint8_t* symbols, uint32_t* end_ok,
                               void* hip_stream);
 
+/* Diagnostics: per-kernel timing of the fused decode-attention kernel.
+ * While enabled, every kvq_decode_attention call records a pair of HIP events
+ * on its stream around that one kernel (the events are created on first use
+ * and reused; up to 4096 launches are held between collects, later launches
+ * are not timed).  kvq_timing_collect waits for the recorded events, returns
+ * the summed milliseconds and the number of timed launches since the previous
+ * collect, and clears them.  Not thread-safe; timing off by default. */
+kvq_status kvq_timing_enable(int on);
+kvq_status kvq_timing_collect(double* total_ms, int64_t* launches);
+
 /* Static description of a status code. */
 const char* kvq_status_str(kvq_status status);
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "device_common.h"
 
@@ -76,9 +77,59 @@ int pick_spw(int64_t n_streams, int n, int C) {
   return 0;
 }
 
+// Opt-in event timing of the fused attention kernel (diagnostics only).
+struct KernelTimer {
+  bool on = false;
+  std::vector<hipEvent_t> start, stop;
+  size_t used = 0;
+  static constexpr size_t kMax = 4096;
+};
+KernelTimer g_timer;
+
+bool timer_begin(hipStream_t stream, size_t* slot) {
+  if (!g_timer.on || g_timer.used >= KernelTimer::kMax) return false;
+  if (g_timer.used == g_timer.start.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return false;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return false;
+    }
+    g_timer.start.push_back(a);
+    g_timer.stop.push_back(b);
+  }
+  *slot = g_timer.used;
+  return hipEventRecord(g_timer.start[*slot], stream) == hipSuccess;
+}
+
+void timer_end(hipStream_t stream, size_t slot) {
+  if (hipEventRecord(g_timer.stop[slot], stream) == hipSuccess) g_timer.used = slot + 1;
+}
+
 }  // namespace
 
 extern "C" {
+
+kvq_status kvq_timing_enable(int on) {
+  g_timer.on = on != 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_timing_collect(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return KVQ_EINVAL;
+  double tot = 0.0;
+  for (size_t i = 0; i < g_timer.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timer.stop[i]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.start[i], g_timer.stop[i]) != hipSuccess)
+      return KVQ_EDEVICE;
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = int64_t(g_timer.used);
+  g_timer.used = 0;
+  return KVQ_OK;
+}
 
 kvq_status kvq_workspace_bytes(const kvq_plan* plan, int op, int64_t n_seqs, int64_t seq_len,
                                int32_t n_q_heads, size_t* bytes) {
@@ -218,7 +269,10 @@ kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q
   aa.tau = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
   std::memcpy(aa.deck, plan->side[0].dec, sizeof(aa.deck));
   std::memcpy(aa.decv, plan->side[1].dec, sizeof(aa.decv));
+  size_t slot = 0;
+  const bool timed = timer_begin(stream, &slot);
   if (kvq::launch_attention(aa, n_seqs, n_q_heads, G, d, stream) != hipSuccess) return KVQ_EDEVICE;
+  if (timed) timer_end(stream, slot);
 
   kvq::CombineArgs ca;
   ca.part = part;

@@ -50,6 +50,8 @@ _SIGS = {
                                     _P, _P, _P, ctypes.c_size_t, _P]),
     "kvq_decode_symbols": (_I32, [_P, ctypes.c_int, _P, _I64, _P, _P, _P]),
     "kvq_status_str": (ctypes.c_char_p, [_I32]),
+    "kvq_timing_enable": (_I32, [ctypes.c_int]),
+    "kvq_timing_collect": (_I32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
 }
 
 
@@ -174,6 +176,17 @@ def kvq_decode_symbols(plan, side, cont, symbols, end_ok=None, stream=None):
     n_streams = cont.numel() // cont.shape[-1]
     _check("kvq_decode_symbols", lib().kvq_decode_symbols(
         plan.handle, side, _ptr(cont), n_streams, _ptr(symbols), _ptr(end_ok), _stream(stream)))
+
+
+def kvq_timing_enable(on):
+    _check("kvq_timing_enable", lib().kvq_timing_enable(int(bool(on))))
+
+
+def kvq_timing_collect():
+    """(total milliseconds, launches) of the timed attention kernels."""
+    ms, n = ctypes.c_double(), _I64()
+    _check("kvq_timing_collect", lib().kvq_timing_collect(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def alloc_cache(plan, n_seqs, seq_len, device="cuda"):
