@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 
-SOURCES = ["plan.cpp", "encode.hip", "decode.hip", "api.hip"]
+SOURCES = ["plan.cpp", "encode.hip", "decode.hip", "attention.hip", "api.hip"]
 
 # -ffp-contract=off: no fused multiply-add may change a rounding the encoder's
 # bit-exact containers depend on.  Denormals are kept (IEEE behaviour).

@@ -9,10 +9,6 @@
 
 #include "device_common.h"
 
-namespace kvq {
-bool attention_supported(int Hq, int G, int d);
-}
-
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -32,18 +28,25 @@ void split_geometry(int64_t S, int64_t T, int* nsplit, int64_t* tokens_per_split
 }
 
 struct WsLayout {
-  size_t qrot, qsum, qmu, part, total;
+  size_t qop, qscale, qsum, qmu, part, total;
 };
 
+// Decode-attention workspace: the fp16 query operand (hi + lo, 16 bytes per
+// 4 channels of a query slot; slots padded to a multiple of 4 per KV head),
+// per-head scale, sum and per-window mean terms, and the split partials.
 WsLayout ws_layout(const kvq_plan* plan, int64_t S, int64_t T, int Hq) {
   int nsplit;
   int64_t tps;
   split_geometry(S, T, &nsplit, &tps);
   const int d = plan->params.head_dim;
+  const int hkv = plan->params.n_kv_heads;
+  const int G = Hq / hkv > 0 ? Hq / hkv : 1;
+  const int slots = ((G + 3) / 4) * 4;
   const int64_t nW = T / plan->params.mean_window;
   WsLayout w;
-  w.qrot = 0;
-  w.qsum = round256(w.qrot + size_t(S) * Hq * d * 4);
+  w.qop = 0;
+  w.qscale = round256(w.qop + size_t(S) * hkv * slots * (d / 4) * 16);
+  w.qsum = round256(w.qscale + size_t(S) * Hq * 4);
   w.qmu = round256(w.qsum + size_t(S) * Hq * 4);
   w.part = round256(w.qmu + size_t(S) * Hq * nW * 4);
   w.total = round256(w.part + size_t(S) * nsplit * Hq * (d + 4) * 4);
@@ -221,7 +224,8 @@ kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q
   if (n_q_heads < 1 || n_q_heads % Hkv) return KVQ_EINVAL;
   if (n_seqs < 1 || seq_len < W || seq_len % W) return KVQ_EINVAL;
   const int G = n_q_heads / Hkv;
-  if (seq_len % 64 || !kvq::attention_supported(n_q_heads, G, d)) return KVQ_EUNSUPPORTED;
+  if (seq_len % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W))
+    return KVQ_EUNSUPPORTED;
   if (n_seqs > 65535) return KVQ_EUNSUPPORTED;
   const WsLayout wl = ws_layout(plan, n_seqs, seq_len, n_q_heads);
   if (workspace_bytes < wl.total) return KVQ_EWORKSPACE;
@@ -230,48 +234,59 @@ kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q
   split_geometry(n_seqs, seq_len, &nsplit, &tps);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* qrot = reinterpret_cast<float*>(ws + wl.qrot);
+  float* qscale = reinterpret_cast<float*>(ws + wl.qscale);
   float* qsum = reinterpret_cast<float*>(ws + wl.qsum);
   float* qmu = reinterpret_cast<float*>(ws + wl.qmu);
   float* part = reinterpret_cast<float*>(ws + wl.part);
 
-  kvq::PrologueArgs pa;
+  kvq::Prologue2Args pa;
   pa.q = static_cast<const uint16_t*>(q);
   pa.mean_q = k_mean_q;
   pa.mean_scale = k_mean_scale;
-  pa.qrot = qrot;
+  pa.qop = reinterpret_cast<uint16_t*>(ws + wl.qop);
+  pa.qscale = qscale;
   pa.qsum = qsum;
   pa.qmu = qmu;
   pa.nW = seq_len / W;
   pa.Hq = n_q_heads;
   pa.G = G;
-  pa.d = d;
   pa.n = plan->n;
   pa.hscale = plan->hadamard_scale;
-  if (kvq::launch_prologue(pa, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
+  if (kvq::launch_prologue2(pa, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
 
-  kvq::AttnArgs aa;
+  kvq::Attn2Args aa;
+  std::memset(&aa, 0, sizeof(aa));
   aa.k_cont = k_cont;
   aa.v_cont = v_cont;
   aa.k_so = k_so;
   aa.v_so = v_so;
-  aa.qrot = qrot;
+  aa.qop = reinterpret_cast<const uint4*>(ws + wl.qop);
+  aa.qscale = qscale;
   aa.qsum = qsum;
   aa.qmu = qmu;
   aa.part = part;
   aa.T = seq_len;
   aa.tokens_per_split = tps;
-  aa.nsplit = nsplit;
   aa.nW = seq_len / W;
-  aa.W = W;
+  aa.nsplit = nsplit;
+  aa.log2W = 0;
+  while ((1 << aa.log2W) < W) ++aa.log2W;
   aa.CK = P.container_bytes_k;
   aa.CV = P.container_bytes_v;
   aa.tau = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
-  std::memcpy(aa.deck, plan->side[0].dec, sizeof(aa.deck));
-  std::memcpy(aa.decv, plan->side[1].dec, sizeof(aa.decv));
+  aa.Mk = P.levels_k;
+  aa.Mv = P.levels_v;
+  for (int m = 0; m < kvq::kMaxLevels; ++m) {
+    aa.fk[m] = plan->side[0].freq[m];
+    aa.ck[m] = plan->side[0].cum[m];
+    aa.hbk[m] = plan->side[0].fp16_hi[m];
+    aa.fv[m] = plan->side[1].freq[m];
+    aa.cv[m] = plan->side[1].cum[m];
+    aa.hbv[m] = plan->side[1].fp16_hi[m];
+  }
   size_t slot = 0;
   const bool timed = timer_begin(stream, &slot);
-  if (kvq::launch_attention(aa, n_seqs, n_q_heads, G, d, stream) != hipSuccess) return KVQ_EDEVICE;
+  if (kvq::launch_attention2(aa, n_seqs, n_q_heads, G, stream) != hipSuccess) return KVQ_EDEVICE;
   if (timed) timer_end(stream, slot);
 
   kvq::CombineArgs ca;

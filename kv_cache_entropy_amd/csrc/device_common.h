@@ -71,35 +71,37 @@ struct DecSymArgs {
   uint32_t dec[256];
 };
 
-struct PrologueArgs {
-  const uint16_t* q;          // bf16 [S, Hq, d]
+struct Prologue2Args {
+  const uint16_t* q;          // bf16 [S, Hq, 128]
   const int8_t* mean_q;       // [S, nW, n]
   const uint16_t* mean_scale; // [S, nW]
-  float* qrot;                // [S, Hq, d]
+  uint16_t* qop;              // fp16 MFMA operand [S][Hkv][ngm][32][4][hi 4, lo 4]
+  float* qscale;              // [S, Hq]: 2^-e undoing the operand scaling
   float* qsum;                // [S, Hq]
   float* qmu;                 // [S, Hq, nW]
   int64_t nW;
-  int Hq, G, d, n;
+  int Hq, G, n;
   float hscale;
 };
 
-struct AttnArgs {
+struct Attn2Args {
   const uint8_t* k_cont;
   const uint8_t* v_cont;
   const uint16_t* k_so;
   const uint16_t* v_so;
-  const float* qrot;
+  const uint4* qop;
+  const float* qscale;
   const float* qsum;
   const float* qmu;
-  float* part;                // [S, nsplit, Hq, d + 4]
+  float* part;                // [S, nsplit, Hq, 128 + 4]
   int64_t T;
   int64_t tokens_per_split;
-  int nsplit;
   int64_t nW;
-  int W, CK, CV;
+  int nsplit, log2W, CK, CV;
   float tau;
-  uint32_t deck[256];
-  uint32_t decv[256];
+  int Mk, Mv;
+  uint32_t fk[kMaxLevels], ck[kMaxLevels], hbk[kMaxLevels];
+  uint32_t fv[kMaxLevels], cv[kMaxLevels], hbv[kMaxLevels];
 };
 
 struct CombineArgs {
@@ -213,8 +215,9 @@ __device__ inline void fwht_lanes(float (&v)[NPL], int d, int lane, float scale)
 hipError_t launch_key_mean(const KeyMeanArgs& a, int64_t n_windows, hipStream_t stream);
 hipError_t launch_encode(const EncodeArgs& a, int64_t n_streams, hipStream_t stream);
 hipError_t launch_decode_symbols(const DecSymArgs& a, hipStream_t stream);
-hipError_t launch_prologue(const PrologueArgs& a, int64_t S, hipStream_t stream);
-hipError_t launch_attention(const AttnArgs& a, int64_t S, int Hq, int G, int d, hipStream_t stream);
+hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t stream);
+hipError_t launch_attention2(const Attn2Args& a, int64_t S, int Hq, int G, hipStream_t stream);
+bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int window);
 hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream);
 
 }  // namespace kvq

@@ -170,6 +170,17 @@ bool build_side(int levels, int n, double alpha, int container_bytes, kvq::SideT
   for (int m = 0; m < levels; ++m)
     for (uint32_t z = s.cum[m]; z < s.cum[m] + s.freq[m]; ++z)
       s.dec[z] = s.freq[m] | ((z - s.cum[m]) << 8) | (uint32_t(m) << 16);
+  for (int m = 0; m < levels; ++m) {
+    // fp16 bit pattern of the integer m: exponent 15 + floor(log2 m), 10-bit mantissa
+    uint32_t bits = 0;
+    if (m > 0) {
+      int e = 0;
+      while ((2 << e) <= m) ++e;
+      const uint32_t mant = (uint32_t(m) << (10 - e)) & 0x3FFu;
+      bits = (uint32_t(15 + e) << 10) | mant;
+    }
+    s.fp16_hi[m] = bits >> 8;
+  }
   uint32_t cheap = 0;
   for (int m = 1; m < levels; ++m)
     if (s.rate_fx[m] < s.rate_fx[cheap]) cheap = m;

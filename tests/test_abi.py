@@ -93,8 +93,8 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert need > 0
     assert L.kvq_decode_attention(plan.handle, a16, 32, a16, a16, a16, a16, a16, a16, 2, 1024, 0.0,
                                   a16, None, a16, need - 1, st) == -6
-    # unsupported head layout
-    assert L.kvq_decode_attention(plan.handle, a16, 16, a16, a16, a16, a16, a16, a16, 1, 1024, 0.0,
+    # unsupported head layout (3 query heads per KV head)
+    assert L.kvq_decode_attention(plan.handle, a16, 24, a16, a16, a16, a16, a16, a16, 1, 1024, 0.0,
                                   a16, None, a16, 1 << 30, st) == -3
     assert L.kvq_decode_symbols(plan.handle, 2, a16, 4, a16, None, st) == -1
     assert plan.workspace_bytes(0, 4, 1024, 32) == 0
