@@ -397,6 +397,227 @@ __global__ __launch_bounds__(64, 2) void attention2_kernel(Attn2Args a) {
       }
 }
 
+
+// ----------------------------------------------------------- attention (v3)
+// Two decode chains per lane: while the K stream of (tile i, KV head g) is
+// decoded and contracted with the query, the V stream of the head before it
+// in (tile, head) order is decoded into the int8 transpose chunk and
+// contracted with that head's softmax weights.  Only one head group of logits
+// is live at a time.  The first iteration's V work and the last iteration's K
+// work are dummies on valid containers (zero weights, discarded logits).
+constexpr int kChunk8Stride = 68;   // bytes per channel row of the int8 V chunk
+
+template <int G, int HKV>
+__global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
+  constexpr int HQ = G * HKV;
+  constexpr int NGM = (G + 3) / 4;
+  constexpr int NW = NGM * 4;
+  __shared__ uint2 tabK[256], tabV[256];
+  __shared__ __align__(16) uint8_t ringK[64 * kRingStride];
+  __shared__ __align__(16) uint8_t ringV[64 * kRingStride];
+  __shared__ __align__(16) uint8_t vch[64 * kChunk8Stride];
+  __shared__ __align__(16) uint16_t wts[2][2][NW][64];   // [buffer][hi/lo][slot][token]
+  __shared__ float runM[HQ], runL[HQ], runZ[HQ];
+  __shared__ float affS[HQ], affQ[HQ], affM[HQ];
+
+  const int lane = threadIdx.x;
+  const int64_t s = blockIdx.y;
+  const int split = blockIdx.x;
+  uint8_t* const rK = ringK + lane * kRingStride;
+  uint8_t* const rV = ringV + lane * kRingStride;
+
+  for (int z = lane; z < 256; z += 64) {
+    uint32_t mk = 0, mv = 0;
+    for (int m = 1; m < a.Mk; ++m) mk = (uint32_t(z) >= a.ck[m]) ? uint32_t(m) : mk;
+    for (int m = 1; m < a.Mv; ++m) mv = (uint32_t(z) >= a.cv[m]) ? uint32_t(m) : mv;
+    tabK[z] = make_uint2(a.fk[mk] | (a.hbk[mk] << 24), uint32_t(z) - a.ck[mk]);
+    tabV[z] = make_uint2(a.fv[mv] | (mv << 24), uint32_t(z) - a.cv[mv]);   // V: level index
+  }
+  for (int h = lane; h < HQ; h += 64) {
+    runM[h] = -__builtin_inff();
+    runL[h] = 0.f;
+    runZ[h] = 0.f;
+  }
+  for (int i = lane; i < 2 * 2 * NW * 64; i += 64) (&wts[0][0][0][0])[i] = 0;
+  __syncthreads();
+
+  // fp16 high bytes of levels 0..7 as a v_perm lookup (low byte is zero)
+  const uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
+  const uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
+
+  float4_t O[HKV][2][NGM];
+#pragma unroll
+  for (int g = 0; g < HKV; ++g)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) O[g][c][m] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t tb = int64_t(split) * a.tokens_per_split;
+  const int64_t te = tb + a.tokens_per_split < a.T ? tb + a.tokens_per_split : a.T;
+  const int64_t NT = (te - tb) / 64;
+  const uint4* qop = a.qop + s * (HKV * NGM * 32 * 4);
+  const float* qscale = a.qscale + s * HQ;
+  const float* qsum = a.qsum + s * HQ;
+  const float* qmu = a.qmu + s * HQ * a.nW;
+  const int qn = lane & 3;
+
+  Ring rk, rv;
+  uint32_t xk = 0, xv = 0;
+  float sk = 0.f, ok = 0.f, svK = 0.f, ovK = 0.f;
+
+  for (int64_t i = 0; i <= NT; ++i) {
+    const bool kreal = i < NT;
+    const int64_t tK = tb + 64 * (kreal ? i : NT - 1);        // K tile (clamped dummy)
+#pragma unroll
+    for (int g = 0; g < HKV; ++g) {
+      if (!kreal && g > 0) break;
+      // ---- stream starts
+      if (g == 0) {
+        const int64_t row = s * a.T + tK + lane;
+        xk = ring_start(rk, rK, a.k_cont + row * a.CK, uint32_t(a.CK));
+        sk = h2f(a.k_so[2 * row]);
+        ok = h2f(a.k_so[2 * row + 1]);
+        svK = h2f(a.v_so[2 * row]);
+        ovK = h2f(a.v_so[2 * row + 1]);
+        const int64_t w = tK >> a.log2W;
+        __syncthreads();
+        for (int h = lane; h < HQ; h += 64) {
+          affS[h] = qscale[h];
+          affQ[h] = qsum[h];
+          affM[h] = qmu[h * a.nW + w];
+        }
+        __syncthreads();
+      }
+      const int vg = (g + HKV - 1) % HKV;                      // V's KV head this iteration
+      if (vg == 0 || (i == 0 && g == 0)) {                     // V starts a container
+        // (the very first iteration always starts one: its V work is the
+        // dummy on tile 0, and the ring must point at valid memory)
+        const int64_t vt = (g == 0) ? i - 1 : i;               // V's tile (-1: dummy on tile 0)
+        const int64_t tV = tb + 64 * (vt < 0 ? 0 : (vt >= NT ? NT - 1 : vt));
+        xv = ring_start(rv, rV, a.v_cont + (s * a.T + tV + lane) * a.CV, uint32_t(a.CV));
+      }
+      const uint16_t* wv = &wts[(i * HKV + g + 1) & 1][0][0][0];   // weights of V's head
+      const uint16_t* wv_lo = wv + NW * 64;
+
+      float4_t D[NGM];
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) D[m] = float4_t{0.f, 0.f, 0.f, 0.f};
+      const uint4* qg = qop + g * (NGM * 32 * 4) + qn;
+      uint4 qa[NGM];
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) qa[m] = qg[(m * 32) * 4];
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll 1
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int blk = ch * 4 + b4;
+          if (b4 & 1) {
+            ring_block<1>(rk, rK);
+            ring_block<1>(rv, rV);
+          } else {
+            ring_block<0>(rk, rK);
+            ring_block<0>(rv, rV);
+          }
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const int c = blk * 4 + cc;
+            const int cn = c + 1 < 32 ? c + 1 : 31;
+            uint4 qb[NGM];
+#pragma unroll
+            for (int m = 0; m < NGM; ++m) qb[m] = qg[(m * 32 + cn) * 4];
+            uint32_t e[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              e[r] = dec_step(xk, rk, tabK, rK);
+              const uint32_t ev = dec_step(xv, rv, tabV, rV);
+              vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 24);
+            }
+            const half4_t B = as_half4(__builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
+                                       __builtin_amdgcn_perm(e[3], e[2], 0x07060302u));
+#pragma unroll
+            for (int m = 0; m < NGM; ++m) {
+              D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(qa[m].x, qa[m].y), B, D[m], 0, 0, 0);
+              D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(qa[m].z, qa[m].w), B, D[m], 0, 0, 0);
+              qa[m] = qb[m];
+            }
+          }
+        }
+        // PV of V's head for the 64 channels of this half
+        __syncthreads();
+#pragma unroll 2
+        for (int tq = 0; tq < 16; ++tq) {
+          const uint32_t idx = *reinterpret_cast<const uint32_t*>(vch + lane * kChunk8Stride + 4 * tq);
+          const uint32_t hb = __builtin_amdgcn_perm(lutHi, lutLo, idx);
+          const half4_t B = as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu),
+                                     __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
+#pragma unroll
+          for (int m = 0; m < NGM; ++m) {
+            const uint2 ah = *reinterpret_cast<const uint2*>(wv + (m * 4 + qn) * 64 + 4 * tq);
+            const uint2 al = *reinterpret_cast<const uint2*>(wv_lo + (m * 4 + qn) * 64 + 4 * tq);
+            O[vg][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah.x, ah.y), B, O[vg][ch][m], 0, 0, 0);
+            O[vg][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[vg][ch][m], 0, 0, 0);
+          }
+        }
+        __syncthreads();
+      }
+      // ---- K head g done: logits -> online softmax -> weights for the next iteration
+      if (kreal) {
+        uint16_t* wk = &wts[(i * HKV + g) & 1][0][0][0];
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+          const int m = v / 4, ii = v % 4;
+          float whi = 0.f, wlo = 0.f;
+          if (v < G) {
+            const int h = g * G + v;
+            const float lg = a.tau * (sk * (D[m][ii] * affS[h]) + ok * affQ[h] + affM[h]);
+            const float tmax = wave_max_f(lg);
+            const float Mo = runM[h], Lo = runL[h], Zo = runZ[h];
+            const float Mn = fmaxf(Mo, tmax);
+            const float al = __expf(Mo - Mn);
+            const float p = __expf(lg - Mn);
+            const float ls = wave_sum_f(p);
+            const float zs = wave_sum_f(p * ovK);
+            __syncthreads();
+            runM[h] = Mn;
+            runL[h] = Lo * al + ls;
+            runZ[h] = Zo * al + zs;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) O[g][c][m][ii] *= al;
+            const float wt = p * svK;
+            const __half hh = __float2half_rn(wt);
+            whi = wt;
+            wlo = wt - __half2float(hh);
+          }
+          wk[v * 64 + lane] = __half_as_ushort(__float2half_rn(whi));
+          wk[NW * 64 + v * 64 + lane] = __half_as_ushort(__float2half_rn(wlo));
+        }
+        __syncthreads();
+      }
+    }
+  }
+
+  float* P = a.part + (s * a.nsplit + split) * int64_t(HQ) * (kD + 4);
+#pragma unroll
+  for (int g = 0; g < HKV; ++g)
+#pragma unroll
+    for (int m = 0; m < NGM; ++m)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int v = m * 4 + ii;
+        if (v < G) {
+          const int h = g * G + v;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) P[h * (kD + 4) + c * 64 + lane] = O[g][c][m][ii];
+          if (lane == 0) {
+            P[h * (kD + 4) + kD] = runM[h];
+            P[h * (kD + 4) + kD + 1] = runL[h];
+            P[h * (kD + 4) + kD + 2] = runZ[h];
+          }
+        }
+      }
+}
+
 }  // namespace
 
 hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t stream) {
@@ -414,7 +635,12 @@ bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int 
 
 template <int G, int HKV>
 static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stream) {
-  hipLaunchKernelGGL((attention2_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
+  // the interleaved kernel keeps V levels as int8 and maps them to fp16 with
+  // an 8-entry lookup, so it serves V alphabets of up to 8 levels
+  if (a.Mv <= 8)
+    hipLaunchKernelGGL((attention3_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attention2_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -83,13 +83,15 @@ def compare_cache(c, stats, refs, p, S):
     assert stats.cpu().numpy().astype(np.uint64).tolist() == tot.tolist()
 
 
-def run_case(name, budget_idx, seqs, tokens):
+def run_case(name, budget_idx, seqs, tokens, w=None, levels=(8, 6)):
     kvq = _kvq()
-    w = synth.WORKLOADS[name]
+    w = w or synth.WORKLOADS[name]
     ck, cv = w.containers[budget_idx]
-    say(f"case {name} budget={w.budgets[budget_idx]} C=({ck},{cv}) seqs={seqs} tokens={tokens}")
-    plan = kvq.Plan(w.n_kv_heads, w.head_dim, 8, 6, ck, cv, 128, 1.4)
-    p = O.OracleParams(w.n_kv_heads, w.head_dim, 8, 6, ck, cv, 128, 1.4)
+    mk, mv = levels
+    say(f"case {w.name} budget={w.budgets[budget_idx]} C=({ck},{cv}) M=({mk},{mv}) "
+        f"heads={w.n_q_heads}/{w.n_kv_heads} seqs={seqs} tokens={tokens}")
+    plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4)
+    p = O.OracleParams(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4)
     k, v = synth.cache_inputs(w, "cuda", seqs, tokens)
     q = synth.queries(w, "cuda", seqs)
     c, stats = gpu_encode(kvq, plan, k, v)
@@ -129,6 +131,19 @@ def test_tiny_full():
 ])
 def test_reduced_configs(name, bi, seqs, tokens):
     run_case(name, bi, seqs, tokens)
+
+
+@pytest.mark.parametrize("hq,hkv,levels,cont", [
+    (8, 4, (8, 6), (180, 130)),      # 2 query heads per KV head
+    (2, 2, (8, 6), (100, 70)),       # one query head per KV head, two KV heads
+    (8, 1, (8, 6), (48, 36)),        # 8 query heads on one KV head (two MFMA groups)
+    (8, 2, (8, 9), (96, 90)),        # 9 V levels: the non-interleaved kernel
+    (4, 4, (6, 4), (150, 100)),      # other alphabets
+])
+def test_other_head_layouts_and_alphabets(hq, hkv, levels, cont):
+    w = synth.Workload(f"layout{hq}x{hkv}", hq, hkv, 128, 2, 1, 640, 11 + hq + hkv, "keymeans",
+                       (cont,), (0.0,))
+    run_case(None, 0, [0, 1], None, w=w, levels=levels)
 
 
 def test_encode_is_deterministic():
