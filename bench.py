@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
-ATTN_SOURCES = ("kv_cache_entropy_amd/csrc/decode.hip", "kv_cache_entropy_amd/csrc/device_common.h")
+ATTN_SOURCES = ("kv_cache_entropy_amd/csrc/attention.hip", "kv_cache_entropy_amd/csrc/device_common.h")
 
 
 def log(*a):
@@ -64,6 +64,8 @@ def main():
     ap.add_argument("--budget", type=float, default=None, help="bits/elem of the workload to run")
     ap.add_argument("--encode-reps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on a single GPU only; --gpus {args.gpus} is not "
@@ -74,6 +76,17 @@ def main():
     from kv_cache_entropy_amd import kvq, synth
 
     dev = "cuda"
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+        # the factor that turns the counters into HBM bytes
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": nbytes, "copies": 3}), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     bi = 0
     if args.budget is not None:
