@@ -131,7 +131,11 @@ kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v
  *   out           [n_seqs, Hq, d] bf16 (round-to-nearest-even of out_f32)
  *   out_f32       nullable [n_seqs, Hq, d] fp32
  *   workspace     device memory of at least kvq_workspace_bytes(plan, 1, ...)
- * Results are deterministic for a given shape. */
+ * Results are deterministic for a given shape.  Returns KVQ_EUNSUPPORTED
+ * unless d = 128, Hkv and Hq / Hkv are in {1, 2, 4, 8}, both alphabets have at
+ * most 9 levels, W >= 64, seq_len is a multiple of 64, n_seqs <= 65535 and
+ * seq_len * max(C_K, C_V) + 16 <= 2^31 - 1; KVQ_EWORKSPACE if the workspace
+ * is too small.  Nothing is launched when an error is returned. */
 kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q_heads,
                                 const uint8_t* k_cont, const uint8_t* v_cont,
                                 const uint16_t* k_so, const uint16_t* v_so,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <algorithm>
+#include <climits>
 #include <cstring>
 #include <vector>
 
@@ -227,6 +229,9 @@ kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q
   if (seq_len % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W))
     return KVQ_EUNSUPPORTED;
   if (n_seqs > 65535) return KVQ_EUNSUPPORTED;
+  // the attention kernel addresses one sequence's containers with 32-bit offsets
+  if (int64_t(seq_len) * std::max(P.container_bytes_k, P.container_bytes_v) + 16 > INT32_MAX)
+    return KVQ_EUNSUPPORTED;
   const WsLayout wl = ws_layout(plan, n_seqs, seq_len, n_q_heads);
   if (workspace_bytes < wl.total) return KVQ_EWORKSPACE;
   int nsplit;

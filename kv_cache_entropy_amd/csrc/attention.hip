@@ -398,50 +398,231 @@ __global__ __launch_bounds__(64, 2) void attention2_kernel(Attn2Args a) {
 }
 
 
-// ----------------------------------------------------------- attention (v3)
-// Two decode chains per lane: while the K stream of (tile i, KV head g) is
+// ----------------------------------------------------------- attention (v4)
+// Same per-wave schedule as a single-wave workgroup on one token range, with
+// two decode chains per lane: while the K stream of (tile i, KV head g) is
 // decoded and contracted with the query, the V stream of the head before it
 // in (tile, head) order is decoded into the int8 transpose chunk and
-// contracted with that head's softmax weights.  Only one head group of logits
-// is live at a time.  The first iteration's V work and the last iteration's K
-// work are dummies on valid containers (zero weights, discarded logits).
-constexpr int kChunk8Stride = 68;   // bytes per channel row of the int8 V chunk
+// contracted with that head's softmax weights.  The first iteration's V work
+// and the last iteration's K work are dummies on valid containers (zero
+// weights, discarded logits).
+//
+// Eight such waves share one workgroup so that they can share decode tables
+// replicated across LDS banks.  LDS map (byte offsets, in this order):
+//   per wave (below 64 KiB, so chunk offsets fold into instructions): V chunk,
+//                softmax weights, running softmax state, the tile's per-head
+//                affine terms
+//   rings        wave w, stream s (K 0, V 1): 17 rows of 64 dwords at
+//                + (2w + s) * 4352; lane l owns dword l of every row
+//   K, V decode tables, R replicas each (R = 16, or 8 when LDS is short)
+// Decode-table entries are 32-bit: f | (z - c) << 8 | payload, the payload
+// being the fp16 high byte of the level in bits 24..31 (K; levels 0..8 have a
+// zero low byte) or the level index in bits 16..23 (V).  Replica r of slot z
+// is dword z*R + r, so it only occupies banks congruent to r mod R (32 banks
+// of 4 bytes); lane l reads replica l mod R.
+// A lane's ring holds container bytes [16 rows of 4]: frame byte p sits in
+// row (p / 4) mod 16, byte p mod 4 of the lane's dword, i.e. always in bank
+// l mod 32, so ring reads and writes never conflict.  Row 16 repeats row 0 so
+// that two consecutive rows can be read with one ds_read2.  The decoder reads
+// the 8-byte window holding the next 4 bytes once per 4 symbols and takes its
+// bytes with v_perm.
+constexpr int kChunk8Stride = 68;     // bytes per channel row of the int8 V chunk
+constexpr int kWaves = 8;
+constexpr uint32_t kRingBytes = 17u * 256u;
 
 template <int G, int HKV>
-__global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
-  constexpr int HQ = G * HKV;
+struct Lay4 {
+  static constexpr int HQ = G * HKV;
+  static constexpr int NW = ((G + 3) / 4) * 4;
+  // per wave, at w * SIZE
+  static constexpr uint32_t VCH = 0;                                // [64 ch][68] int8 levels
+  static constexpr uint32_t WTS = 64u * kChunk8Stride;              // [hi/lo][NW][64] fp16
+  static constexpr uint32_t RUN = WTS + 2u * NW * 64u * 2u;         // 6 x [HQ] f32
+  static constexpr uint32_t SIZE = (RUN + 6u * HQ * 4u + 15u) & ~15u;
+  static constexpr uint32_t RINGS = (kWaves * SIZE + 255u) & ~255u;
+  static constexpr uint32_t RING_END = RINGS + 2u * kWaves * kRingBytes;
+  static constexpr uint32_t REPS = RING_END + 2u * 256u * 16u * 4u <= 163840u ? 16u : 8u;
+  static constexpr uint32_t TAB_BYTES = 256u * REPS * 4u;
+  static constexpr uint32_t TABK = (RING_END + TAB_BYTES - 1u) / TAB_BYTES * TAB_BYTES;
+  static constexpr uint32_t TABV = TABK + TAB_BYTES;
+  static constexpr uint32_t TOTAL = TABV + TAB_BYTES;
+  static constexpr uint32_t SLOT_SHIFT = REPS == 16u ? 6u : 5u;     // log2(REPS * 4)
+  static_assert(kWaves * SIZE <= 65536u, "per-wave regions must sit below 64 KiB");
+  static_assert(TOTAL <= 163840u, "exceeds the LDS of a CU");
+};
+
+__device__ inline void wave_lds_fence() {
+  // LDS instructions of one wave execute in order; this only keeps the
+  // compiler from moving LDS accesses across the point.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Hides a value's known bits from the optimiser, so that an or with it stays
+// an or (one v_and_or_b32) and a product stays a product (byte-select operands).
+__device__ inline uint32_t opaque(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// Container bytes are fetched with raw buffer loads on a resource spanning the
+// wave's sequence; a lane with nothing to fetch passes an offset past the end,
+// which loads zeros without touching memory, so every lane issues the same
+// loads and the outstanding-load count stays static.
+constexpr uint32_t kNoLoad = 0x80000000u;
+
+__device__ inline __amdgpu_buffer_rsrc_t seq_rsrc(const uint8_t* seq_base, uint32_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(seq_base);
+  const uint32_t mis = uint32_t(a & 15u);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(seq_base - mis), 0, int(bytes + mis),
+                                           0x00020000);
+}
+
+__device__ inline uint4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+struct Ring5 {
+  uint32_t fo;          // buffer offset of the lane's 16-byte aligned frame
+  uint32_t off;         // LDS offset of the lane's dword in row 0 of its ring
+  uint32_t P;           // frame position of the next unread byte
+  uint32_t F;           // frame position of the next chunk to fetch
+  uint32_t lim;         // frame position one past the container's last byte
+  uint4 pend[2];        // chunks in flight
+  uint32_t ppos[2];     // their frame positions (kNoChunk: nothing to write)
+};
+
+__device__ inline uint32_t ring5_row(uint32_t pos, uint32_t off) {
+  return (__builtin_amdgcn_ubfe(pos, 2u, 4u) << 8) + off;    // row (pos / 4) mod 16
+}
+
+// Writes the 16-byte chunk at frame position pos (a multiple of 16, so its
+// four rows do not wrap), and row 16 with it when it lands on row 0.
+__device__ inline void ring5_write(uint8_t* lds, uint32_t off, uint32_t pos, const uint4& d) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(lds + ring5_row(pos, off));
+  w[0] = d.x;
+  w[64] = d.y;
+  w[128] = d.z;
+  w[192] = d.w;
+  if ((pos & 63u) == 0u) w[1024] = d.x;
+}
+
+// Bytes P .. P+3 of the stream (P's 8-byte window, shifted by P mod 4).
+__device__ inline uint32_t ring5_window(const Ring5& r, const uint8_t* lds) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(lds + ring5_row(r.P, r.off));
+  return __builtin_amdgcn_alignbyte(w[64], w[0], r.P);
+}
+
+// Starts a container (cont_off: its byte offset in the sequence's buffer
+// resource): fills the ring with the first 64 frame bytes (chunks past the
+// container are not fetched) and reads the 4-byte little-endian initial state.
+__device__ inline uint32_t ring5_start(Ring5& r, uint8_t* lds, __amdgpu_buffer_rsrc_t rs, uint32_t cont_off,
+                                       uint32_t C) {
+  const uint32_t off0 = cont_off & 15u;
+  r.fo = cont_off - off0;
+  r.lim = off0 + C;
+  uint4 d[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = load_chunk(rs, uint32_t(16 * q) < r.lim ? r.fo + 16u * q : kNoLoad);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ring5_write(lds, r.off, 16u * q, d[q]);
+  r.F = 64u;
+  r.ppos[0] = r.ppos[1] = kNoChunk;
+  r.P = off0;
+  const uint32_t x = ring5_window(r, lds);
+  r.P = off0 + 4u;
+  return x;
+}
+
+// Once per 16 symbols, slot S alternating: write the chunk fetched two blocks
+// ago, then fetch the next chunk if the lane is within 48 bytes of the fetch
+// front.  Invariants (at most one byte per symbol): the bytes of the coming 16
+// symbols are written before they are read, and a chunk never overwrites
+// bytes not yet consumed.
+template <int S>
+__device__ inline void ring5_block(Ring5& r, uint8_t* lds, __amdgpu_buffer_rsrc_t rs) {
+  if (r.ppos[S] != kNoChunk) ring5_write(lds, r.off, r.ppos[S], r.pend[S]);
+  const bool real = (r.F < r.lim) && (r.F - r.P <= 48u);
+  r.pend[S] = load_chunk(rs, real ? r.fo + r.F : kNoLoad);
+  r.ppos[S] = real ? r.F : kNoChunk;
+  r.F += real ? 16u : 0u;
+}
+
+// Selector of v_perm that yields (x << 8) | byte j of the window (j = low byte).
+constexpr uint32_t kSel0 = 0x06050400u;
+
+// One symbol of Algorithm 2: x = f (x >> 8) + z - c, then at most one byte
+// shifted in.  win holds the next 4 stream bytes and sel counts those already
+// taken in the current group of 4 symbols, so the update is branch-free and
+// reads no LDS besides the table.  Returns the table entry.
+template <uint32_t SLOT_SHIFT>
+__device__ inline uint32_t dec5_step(uint32_t& x, uint32_t win, uint32_t& sel, const uint8_t* lds, uint32_t toff) {
+  constexpr uint32_t mask = 0xFFu << SLOT_SHIFT;
+  const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + (((x << SLOT_SHIFT) & mask) | toff));
+  const uint32_t m = opaque(__umul24(e & 0xFFu, x >> 8));
+  x = m + ((e >> 8) & 0xFFu);
+  const bool renorm = x < kStateLow;
+  const uint32_t xs = __builtin_amdgcn_perm(x, win, sel);
+  x = renorm ? xs : x;
+  sel = opaque(sel + (renorm ? 1u : 0u));
+  return e;
+}
+
+template <int G, int HKV>
+__global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a, int64_t S) {
+  using Lay = Lay4<G, HKV>;
+  constexpr int HQ = Lay::HQ;
   constexpr int NGM = (G + 3) / 4;
-  constexpr int NW = NGM * 4;
-  __shared__ uint2 tabK[256], tabV[256];
-  __shared__ __align__(16) uint8_t ringK[64 * kRingStride];
-  __shared__ __align__(16) uint8_t ringV[64 * kRingStride];
-  __shared__ __align__(16) uint8_t vch[64 * kChunk8Stride];
-  __shared__ __align__(16) uint16_t wts[2][2][NW][64];   // [buffer][hi/lo][slot][token]
-  __shared__ float runM[HQ], runL[HQ], runZ[HQ];
-  __shared__ float affS[HQ], affQ[HQ], affM[HQ];
+  constexpr int NW = Lay::NW;
+  __shared__ __align__(16) uint8_t lds[Lay::TOTAL];
 
-  const int lane = threadIdx.x;
-  const int64_t s = blockIdx.y;
-  const int split = blockIdx.x;
-  uint8_t* const rK = ringK + lane * kRingStride;
-  uint8_t* const rV = ringV + lane * kRingStride;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  for (int z = lane; z < 256; z += 64) {
+  // decode tables, shared by the workgroup
+  for (int idx = tid; idx < 256 * int(Lay::REPS); idx += 64 * kWaves) {
+    const uint32_t z = uint32_t(idx) / Lay::REPS;
     uint32_t mk = 0, mv = 0;
-    for (int m = 1; m < a.Mk; ++m) mk = (uint32_t(z) >= a.ck[m]) ? uint32_t(m) : mk;
-    for (int m = 1; m < a.Mv; ++m) mv = (uint32_t(z) >= a.cv[m]) ? uint32_t(m) : mv;
-    tabK[z] = make_uint2(a.fk[mk] | (a.hbk[mk] << 24), uint32_t(z) - a.ck[mk]);
-    tabV[z] = make_uint2(a.fv[mv] | (mv << 24), uint32_t(z) - a.cv[mv]);   // V: level index
+    for (int m = 1; m < a.Mk; ++m) mk = (z >= a.ck[m]) ? uint32_t(m) : mk;
+    for (int m = 1; m < a.Mv; ++m) mv = (z >= a.cv[m]) ? uint32_t(m) : mv;
+    reinterpret_cast<uint32_t*>(lds + Lay::TABK)[idx] = a.fk[mk] | ((z - a.ck[mk]) << 8) | (a.hbk[mk] << 24);
+    reinterpret_cast<uint32_t*>(lds + Lay::TABV)[idx] = a.fv[mv] | ((z - a.cv[mv]) << 8) | (mv << 16);
   }
+  __syncthreads();
+
+  const int64_t gw = int64_t(blockIdx.x) * kWaves + w;
+  if (gw >= S * a.nsplit) return;          // (no workgroup barrier follows)
+  const int64_t s = gw / a.nsplit;
+  const int split = int(gw - s * a.nsplit);
+
+  uint8_t* const mine = lds + uint32_t(w) * Lay::SIZE;
+  uint8_t* const vch = mine + Lay::VCH;
+  uint16_t* const wts = reinterpret_cast<uint16_t*>(mine + Lay::WTS);    // [hi/lo][NW][64]
+  float* const runM = reinterpret_cast<float*>(mine + Lay::RUN);
+  float* const runL = runM + HQ;
+  float* const runZ = runL + HQ;
+  float* const affS = runZ + HQ;
+  float* const affQ = affS + HQ;
+  float* const affM = affQ + HQ;
   for (int h = lane; h < HQ; h += 64) {
     runM[h] = -__builtin_inff();
     runL[h] = 0.f;
     runZ[h] = 0.f;
   }
-  for (int i = lane; i < 2 * 2 * NW * 64; i += 64) (&wts[0][0][0][0])[i] = 0;
-  __syncthreads();
+  for (int i = lane; i < 2 * NW * 64; i += 64) wts[i] = 0;
 
-  // fp16 high bytes of levels 0..7 as a v_perm lookup (low byte is zero)
+  const uint32_t toffK = opaque(Lay::TABK + uint32_t(lane % Lay::REPS) * 4u);
+  const uint32_t toffV = opaque(Lay::TABV + uint32_t(lane % Lay::REPS) * 4u);
+  Ring5 rk, rv;
+  rk.off = opaque(Lay::RINGS + uint32_t(2 * w) * kRingBytes + uint32_t(lane) * 4u);
+  rv.off = opaque(Lay::RINGS + uint32_t(2 * w + 1) * kRingBytes + uint32_t(lane) * 4u);
+  wave_lds_fence();
+
+  // fp16 high bytes of V levels 0..7 as a v_perm lookup (low byte is zero)
   const uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
   const uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
 
@@ -461,10 +642,18 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
   const float* qsum = a.qsum + s * HQ;
   const float* qmu = a.qmu + s * HQ * a.nW;
   const int qn = lane & 3;
+  const uint16_t* const wv = wts;                 // weights of the head whose V is decoded
+  const uint16_t* const wv_lo = wts + NW * 64;
 
-  Ring rk, rv;
   uint32_t xk = 0, xv = 0;
   float sk = 0.f, ok = 0.f, svK = 0.f, ovK = 0.f;
+  // buffer resources over this sequence's containers (T C < 2^31, checked by the host)
+  const uint8_t* const kseq = a.k_cont + s * a.T * a.CK;
+  const uint8_t* const vseq = a.v_cont + s * a.T * a.CV;
+  const __amdgpu_buffer_rsrc_t rsK = seq_rsrc(kseq, uint32_t(a.T * a.CK));
+  const __amdgpu_buffer_rsrc_t rsV = seq_rsrc(vseq, uint32_t(a.T * a.CV));
+  const uint32_t misK = uint32_t(reinterpret_cast<uintptr_t>(kseq) & 15u);
+  const uint32_t misV = uint32_t(reinterpret_cast<uintptr_t>(vseq) & 15u);
 
   for (int64_t i = 0; i <= NT; ++i) {
     const bool kreal = i < NT;
@@ -475,19 +664,18 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
       // ---- stream starts
       if (g == 0) {
         const int64_t row = s * a.T + tK + lane;
-        xk = ring_start(rk, rK, a.k_cont + row * a.CK, uint32_t(a.CK));
+        xk = ring5_start(rk, lds, rsK, misK + uint32_t(tK + lane) * uint32_t(a.CK), uint32_t(a.CK));
         sk = h2f(a.k_so[2 * row]);
         ok = h2f(a.k_so[2 * row + 1]);
         svK = h2f(a.v_so[2 * row]);
         ovK = h2f(a.v_so[2 * row + 1]);
-        const int64_t w = tK >> a.log2W;
-        __syncthreads();
+        const int64_t wdx = tK >> a.log2W;
         for (int h = lane; h < HQ; h += 64) {
           affS[h] = qscale[h];
           affQ[h] = qsum[h];
-          affM[h] = qmu[h * a.nW + w];
+          affM[h] = qmu[h * a.nW + wdx];
         }
-        __syncthreads();
+        wave_lds_fence();
       }
       const int vg = (g + HKV - 1) % HKV;                      // V's KV head this iteration
       if (vg == 0 || (i == 0 && g == 0)) {                     // V starts a container
@@ -495,10 +683,8 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
         // dummy on tile 0, and the ring must point at valid memory)
         const int64_t vt = (g == 0) ? i - 1 : i;               // V's tile (-1: dummy on tile 0)
         const int64_t tV = tb + 64 * (vt < 0 ? 0 : (vt >= NT ? NT - 1 : vt));
-        xv = ring_start(rv, rV, a.v_cont + (s * a.T + tV + lane) * a.CV, uint32_t(a.CV));
+        xv = ring5_start(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
       }
-      const uint16_t* wv = &wts[(i * HKV + g + 1) & 1][0][0][0];   // weights of V's head
-      const uint16_t* wv_lo = wv + NW * 64;
 
       float4_t D[NGM];
 #pragma unroll
@@ -513,11 +699,11 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
         for (int b4 = 0; b4 < 4; ++b4) {
           const int blk = ch * 4 + b4;
           if (b4 & 1) {
-            ring_block<1>(rk, rK);
-            ring_block<1>(rv, rV);
+            ring5_block<1>(rk, lds, rsK);
+            ring5_block<1>(rv, lds, rsV);
           } else {
-            ring_block<0>(rk, rK);
-            ring_block<0>(rv, rV);
+            ring5_block<0>(rk, lds, rsK);
+            ring5_block<0>(rv, lds, rsV);
           }
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
@@ -527,12 +713,16 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
 #pragma unroll
             for (int m = 0; m < NGM; ++m) qb[m] = qg[(m * 32 + cn) * 4];
             uint32_t e[4];
+            const uint32_t winK = ring5_window(rk, lds), winV = ring5_window(rv, lds);
+            uint32_t selk = kSel0, selv = kSel0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              e[r] = dec_step(xk, rk, tabK, rK);
-              const uint32_t ev = dec_step(xv, rv, tabV, rV);
-              vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 24);
+              e[r] = dec5_step<Lay::SLOT_SHIFT>(xk, winK, selk, lds, toffK);
+              const uint32_t ev = dec5_step<Lay::SLOT_SHIFT>(xv, winV, selv, lds, toffV);
+              vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
             }
+            rk.P += selk - kSel0;
+            rv.P += selv - kSel0;
             const half4_t B = as_half4(__builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
                                        __builtin_amdgcn_perm(e[3], e[2], 0x07060302u));
 #pragma unroll
@@ -544,7 +734,7 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
           }
         }
         // PV of V's head for the 64 channels of this half
-        __syncthreads();
+        wave_lds_fence();
 #pragma unroll 2
         for (int tq = 0; tq < 16; ++tq) {
           const uint32_t idx = *reinterpret_cast<const uint32_t*>(vch + lane * kChunk8Stride + 4 * tq);
@@ -559,11 +749,11 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
             O[vg][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[vg][ch][m], 0, 0, 0);
           }
         }
-        __syncthreads();
+        wave_lds_fence();
       }
       // ---- K head g done: logits -> online softmax -> weights for the next iteration
       if (kreal) {
-        uint16_t* wk = &wts[(i * HKV + g) & 1][0][0][0];
+        uint16_t* const wk = wts;
 #pragma unroll
         for (int v = 0; v < NW; ++v) {
           const int m = v / 4, ii = v % 4;
@@ -578,7 +768,6 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
             const float p = __expf(lg - Mn);
             const float ls = wave_sum_f(p);
             const float zs = wave_sum_f(p * ovK);
-            __syncthreads();
             runM[h] = Mn;
             runL[h] = Lo * al + ls;
             runZ[h] = Zo * al + zs;
@@ -592,7 +781,7 @@ __global__ __launch_bounds__(64, 2) void attention3_kernel(Attn2Args a) {
           wk[v * 64 + lane] = __half_as_ushort(__float2half_rn(whi));
           wk[NW * 64 + v * 64 + lane] = __half_as_ushort(__float2half_rn(wlo));
         }
-        __syncthreads();
+        wave_lds_fence();
       }
     }
   }
@@ -637,8 +826,11 @@ template <int G, int HKV>
 static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stream) {
   // the interleaved kernel keeps V levels as int8 and maps them to fp16 with
   // an 8-entry lookup, so it serves V alphabets of up to 8 levels
-  if (a.Mv <= 8)
-    hipLaunchKernelGGL((attention3_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
+  if (a.Mv <= 8) {
+    const int64_t waves = S * a.nsplit;
+    hipLaunchKernelGGL((attention4_kernel<G, HKV>), dim3(unsigned((waves + kWaves - 1) / kWaves)),
+                       dim3(64 * kWaves), 0, stream, a, S);
+  }
   else
     hipLaunchKernelGGL((attention2_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
   return hipGetLastError();
