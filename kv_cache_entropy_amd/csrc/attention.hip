@@ -6,26 +6,24 @@
 // let the contractions run on the raw levels with the affine terms applied
 // afterwards.
 //
-// Layout of one workgroup (a single wave, 64 lanes) handling a token range of
-// one sequence in 64-token tiles, lane t <-> token t0 + t:
-//   * Container bytes reach the decoder through a 64-byte ring per lane in
-//     LDS, refilled with 16-byte aligned global loads issued two 16-symbol
-//     blocks before they are needed (a lane consumes at most one byte per
-//     symbol), so only 4 KiB of LDS per wave holds compressed bytes.
-//   * The 256-entry decode table lives in LDS as 8-byte entries:
-//       lo = f | fp16(level) high byte << 24   (bits 8..23 clear)
-//       hi = z - c
-//     so one v_mad_u32_u24 performs x = f (x >> 8) + z - c, and the fp16 level
-//     (levels 0..8 have a zero low byte) sits in the upper half of lo.
+// Two kernels share the same per-wave schedule: one wave handles a token range
+// of one sequence in 64-token tiles, lane t <-> token t0 + t.
 //   * QK^T: every 4 decoded K levels of a lane form the B operand of a
 //     v_mfma_f32_4x4x4f16 block (16 blocks of 4 tokens); the A operand is the
 //     rotated query of 4 heads, split into fp16 hi + lo parts after a
 //     power-of-two scaling, so each lane ends with its own token's logits.
-//   * PV: V levels are written as fp16 into a [64 channels][64 tokens] LDS
-//     chunk; the contraction over tokens is again 4x4x4 MFMA blocks (16
-//     channel groups x 4 heads) with the softmax weights (hi + lo) as A.
+//   * PV: V levels go to a [channel][token] LDS chunk; the contraction over
+//     tokens is again 4x4x4 MFMA blocks (16 channel groups x 4 heads) with the
+//     softmax weights (hi + lo) as A.
 //   * Online softmax per query head across tiles; the per-token scale folds
 //     into the weights and the per-token offset into a separate sum (Eq. 9).
+// attention4_kernel (V alphabets of up to 8 levels) runs eight such waves per
+// workgroup with two decode chains per lane, bank-confined LDS rings and
+// replicated decode tables; its layout is described above its definition.
+// attention2_kernel is the single-wave form for 9-level V alphabets: 8-byte
+// decode-table entries (lo = f | fp16 level high byte << 24, hi = z - c, one
+// v_mad_u32_u24 per symbol), a 64-byte ring per lane refilled by 16-byte loads
+// two 16-symbol blocks ahead, and an fp16 V chunk.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -398,7 +396,7 @@ __global__ __launch_bounds__(64, 2) void attention2_kernel(Attn2Args a) {
 }
 
 
-// ----------------------------------------------------------- attention (v4)
+// ------------------------------------------- attention, eight waves per workgroup
 // Same per-wave schedule as a single-wave workgroup on one token range, with
 // two decode chains per lane: while the K stream of (tile i, KV head g) is
 // decoded and contracted with the query, the V stream of the head before it
