@@ -136,6 +136,40 @@ __device__ inline float wave_sum_f(float v) {
   return v;
 }
 
+// Wave-wide reductions in VALU only: DPP within rows of 16 lanes, then the
+// gfx950 row and half-wave swaps; the result is taken from lane 0 so that it
+// is exactly uniform (the partial sums are combined in lane-dependent order).
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float swap_rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float r = __uint_as_float(a[0]) + __uint_as_float(a[1]);    // own + partner row
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(r), __float_as_uint(r), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);             // own + partner half
+}
+__device__ inline float swap_rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float r = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(r), __float_as_uint(r), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);      // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);      // quad_perm [2,3,0,1]
+  v += dpp_f<0x124>(v);     // row_ror:4
+  v += dpp_f<0x128>(v);     // row_ror:8
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(swap_rows_sum(v))));
+}
+__device__ inline float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(swap_rows_max(v))));
+}
+
 // ------------------------------------------------------------------ prologue
 // One wave per (sequence, KV head, query slot v): slot v < G is query head
 // g G + v; slots up to the next multiple of 4 are zero padding.  Writes the
@@ -759,13 +793,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
           if (v < G) {
             const int h = g * G + v;
             const float lg = a.tau * (sk * (D[m][ii] * affS[h]) + ok * affQ[h] + affM[h]);
-            const float tmax = wave_max_f(lg);
+            const float tmax = wave_max_dpp(lg);
             const float Mo = runM[h], Lo = runL[h], Zo = runZ[h];
             const float Mn = fmaxf(Mo, tmax);
             const float al = __expf(Mo - Mn);
             const float p = __expf(lg - Mn);
-            const float ls = wave_sum_f(p);
-            const float zs = wave_sum_f(p * ovK);
+            const float ls = wave_sum_dpp(p);
+            const float zs = wave_sum_dpp(p * ovK);
             runM[h] = Mn;
             runL[h] = Lo * al + ls;
             runZ[h] = Zo * al + zs;
