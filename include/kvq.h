@@ -94,8 +94,10 @@ kvq_status kvq_containers_for_budget(double bits_per_elem, int32_t n_kv_heads,
                                      int32_t head_dim, int32_t mean_window,
                                      int32_t* c_k, int32_t* c_v);
 
-/* Device workspace needed by kvq_decode_attention (op = 1) for the given
- * shape; op = 0 (encode) needs none and reports 0. */
+/* Device workspace needed by kvq_decode_attention / kvq_decode_attention_ex
+ * (op = 1) for n_seqs sequences of seq_len compressed tokens (seq_len >= 0;
+ * the size also covers an uncompressed tail); op = 0 (encode) needs none and
+ * reports 0. */
 kvq_status kvq_workspace_bytes(const kvq_plan* plan, int op, int64_t n_seqs,
                                int64_t seq_len, int32_t n_q_heads, size_t* bytes);
 
@@ -122,6 +124,25 @@ kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v
                               int8_t* k_mean_q, uint16_t* k_mean_scale,
                               uint64_t* stats, void* hip_stream);
 
+/* Streaming append ([D-Quant] §5.1 "Implementation details": the most recent
+ * tokens stay uncompressed in bf16 and are compressed a window at a time).
+ * Encodes n_tokens tokens per sequence, k, v [n_seqs, n_tokens, Hkv, d], into
+ * rows [token_offset, token_offset + n_tokens) of cache arrays that hold
+ * cache_capacity tokens per sequence (k_cont [n_seqs, cache_capacity, C_K],
+ * k_mean_q [n_seqs, cache_capacity / W, n], ...); other rows are untouched.
+ * n_tokens, token_offset and cache_capacity must be multiples of W
+ * (KVQ_EINVAL otherwise, and for token_offset + n_tokens > cache_capacity).
+ * Every key-mean window lies inside the appended tokens, so appending a
+ * sequence window by window writes exactly the bytes kvq_encode_streams
+ * writes for the whole sequence.  stats as for kvq_encode_streams. */
+kvq_status kvq_encode_append(const kvq_plan* plan, const void* k, const void* v,
+                             kvq_dtype in_dtype, int64_t n_seqs, int64_t n_tokens,
+                             int64_t cache_capacity, int64_t token_offset,
+                             uint8_t* k_cont, uint8_t* v_cont,
+                             uint16_t* k_so, uint16_t* v_so,
+                             int8_t* k_mean_q, uint16_t* k_mean_scale,
+                             uint64_t* stats, void* hip_stream);
+
 /* Read side ([D-Quant] §4.5 "Decoding", Appendix A Algorithm 2 and
  * Eqs. (7)-(9)): one decode query per sequence attends over all seq_len
  * cached tokens; query head h reads KV head h / (Hq / Hkv).
@@ -144,6 +165,29 @@ kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q
                                 void* out, float* out_f32,
                                 void* workspace, size_t workspace_bytes,
                                 void* hip_stream);
+
+/* Decode attention over a compressed prefix and an uncompressed bf16 tail
+ * ([D-Quant] §5.1 "Implementation details": the most recent tokens are kept in
+ * BF16; both parts join one softmax).  The query attends over
+ *   * rows [0, n_tokens) of cache arrays holding cache_capacity tokens per
+ *     sequence (n_tokens a multiple of W and of 64; may be 0, and then the
+ *     cache pointers may be NULL), and
+ *   * rows [0, res_len) of res_k, res_v [n_seqs, res_capacity, Hkv, d] bf16
+ *     (res_len may be 0, and then res_k / res_v may be NULL),
+ * with n_tokens + res_len >= 1.  The workspace is
+ * kvq_workspace_bytes(plan, 1, n_seqs, n_tokens, n_q_heads).  Other arguments
+ * and errors as for kvq_decode_attention, which is this call with
+ * cache_capacity = n_tokens = seq_len and res_len = 0. */
+kvq_status kvq_decode_attention_ex(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                                   const uint8_t* k_cont, const uint8_t* v_cont,
+                                   const uint16_t* k_so, const uint16_t* v_so,
+                                   const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                                   int64_t n_seqs, int64_t cache_capacity, int64_t n_tokens,
+                                   const void* res_k, const void* res_v,
+                                   int64_t res_capacity, int64_t res_len,
+                                   float softmax_scale, void* out, float* out_f32,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* hip_stream);
 
 /* Decodes containers back to symbol indices (Appendix A, Algorithm 2); a
  * verification helper.  side 0 = K table, 1 = V table.

@@ -18,9 +18,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Split-K geometry of the decode attention: 64-token tiles; enough splits to
-// give the chip about 2048 workgroups.
+// give the chip about 2048 waves (each split is one wave).
 void split_geometry(int64_t S, int64_t T, int* nsplit, int64_t* tokens_per_split) {
   const int64_t tiles = T / 64;
+  if (tiles == 0) {
+    *nsplit = 0;
+    *tokens_per_split = 0;
+    return;
+  }
   int64_t want = (2048 + S - 1) / S;
   if (want < 1) want = 1;
   if (want > tiles) want = tiles;
@@ -51,7 +56,8 @@ WsLayout ws_layout(const kvq_plan* plan, int64_t S, int64_t T, int Hq) {
   w.qsum = round256(w.qscale + size_t(S) * Hq * 4);
   w.qmu = round256(w.qsum + size_t(S) * Hq * 4);
   w.part = round256(w.qmu + size_t(S) * Hq * nW * 4);
-  w.total = round256(w.part + size_t(S) * nsplit * Hq * (d + 4) * 4);
+  // one more split per sequence holds the partials of an uncompressed residual
+  w.total = round256(w.part + size_t(S) * (nsplit + 1) * Hq * (d + 4) * 4);
   return w;
 }
 
@@ -75,10 +81,11 @@ kvq::EncTabs enc_tabs(const kvq_plan* plan, int side) {
 }
 
 // Streams per encode workgroup: the largest of 32/16/8/4 that divides the
-// stream count and keeps the symbol and container staging under 56 KiB.
-int pick_spw(int64_t n_streams, int n, int C) {
+// tokens per sequence (a workgroup's streams then lie in one sequence) and
+// keeps the symbol and container staging under 56 KiB.
+int pick_spw(int64_t tokens, int n, int C) {
   for (int spw = 32; spw >= 4; spw >>= 1)
-    if (n_streams % spw == 0 && size_t(spw) * (size_t(n) + size_t(C)) <= 56u * 1024u) return spw;
+    if (tokens % spw == 0 && size_t(spw) * (size_t(n) + size_t(C)) <= 56u * 1024u) return spw;
   return 0;
 }
 
@@ -138,7 +145,7 @@ kvq_status kvq_timing_collect(double* total_ms, int64_t* launches) {
 
 kvq_status kvq_workspace_bytes(const kvq_plan* plan, int op, int64_t n_seqs, int64_t seq_len,
                                int32_t n_q_heads, size_t* bytes) {
-  if (!plan || !bytes || n_seqs < 1 || seq_len < 1) return KVQ_EINVAL;
+  if (!plan || !bytes || n_seqs < 1 || seq_len < 0) return KVQ_EINVAL;
   if (op == 0) {
     *bytes = 0;
     return KVQ_OK;
@@ -148,11 +155,17 @@ kvq_status kvq_workspace_bytes(const kvq_plan* plan, int op, int64_t n_seqs, int
   return KVQ_OK;
 }
 
-kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v,
-                              kvq_dtype in_dtype, int64_t n_seqs, int64_t seq_len,
-                              uint8_t* k_cont, uint8_t* v_cont, uint16_t* k_so, uint16_t* v_so,
-                              int8_t* k_mean_q, uint16_t* k_mean_scale, uint64_t* stats,
-                              void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Encodes n_tokens tokens per sequence (k, v: [S, n_tokens, Hkv, d]) into
+// cache rows [t_off, t_off + n_tokens) of arrays holding `capacity` tokens per
+// sequence.  Every key-mean window is local to the tokens encoded with it.
+kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_dtype in_dtype,
+                       int64_t n_seqs, int64_t n_tokens, int64_t capacity, int64_t t_off,
+                       uint8_t* k_cont, uint8_t* v_cont, uint16_t* k_so, uint16_t* v_so,
+                       int8_t* k_mean_q, uint16_t* k_mean_scale, uint64_t* stats, void* hip_stream) {
   if (!plan || !k || !v || !k_cont || !v_cont || !k_so || !v_so || !k_mean_q || !k_mean_scale)
     return KVQ_EINVAL;
   if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return KVQ_EINVAL;
@@ -163,11 +176,12 @@ kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v
   const kvq_params& P = plan->params;
   const int n = plan->n;
   const int W = P.mean_window;
-  if (n_seqs < 1 || seq_len < W || seq_len % W) return KVQ_EINVAL;
-  if (n % 64 || n > 4096) return KVQ_EUNSUPPORTED;
-  const int64_t n_streams = n_seqs * seq_len;
-  const int spw_k = pick_spw(n_streams, n, P.container_bytes_k);
-  const int spw_v = pick_spw(n_streams, n, P.container_bytes_v);
+  if (n_seqs < 1 || n_tokens < W || n_tokens % W) return KVQ_EINVAL;
+  if (t_off < 0 || t_off % W || capacity % W || t_off + n_tokens > capacity) return KVQ_EINVAL;
+  if (n % 64 || n > 4096 || W < 4) return KVQ_EUNSUPPORTED;
+  const int64_t n_streams = n_seqs * n_tokens;
+  const int spw_k = pick_spw(n_tokens, n, P.container_bytes_k);
+  const int spw_v = pick_spw(n_tokens, n, P.container_bytes_v);
   if (!spw_k || !spw_v) return KVQ_EUNSUPPORTED;
   if (n_streams / 4 > int64_t(0x7FFFFFFF)) return KVQ_EUNSUPPORTED;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -177,12 +191,14 @@ kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v
   km.in_bf16 = in_dtype == KVQ_BF16;
   km.mean_q = k_mean_q;
   km.mean_scale = k_mean_scale;
-  km.T = seq_len;
+  km.T = n_tokens;
+  km.T_cap = capacity;
+  km.t_off = t_off;
   km.W = W;
   km.n = n;
   km.d = P.head_dim;
   km.hscale = plan->hadamard_scale;
-  if (kvq::launch_key_mean(km, n_seqs * (seq_len / W), stream) != hipSuccess) return KVQ_EDEVICE;
+  if (kvq::launch_key_mean(km, n_seqs * (n_tokens / W), stream) != hipSuccess) return KVQ_EDEVICE;
 
   for (int side = 0; side < 2; ++side) {
     kvq::EncodeArgs ea;
@@ -195,7 +211,9 @@ kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v
     ea.cont = side == 0 ? k_cont : v_cont;
     ea.so = side == 0 ? k_so : v_so;
     ea.stats = stats ? reinterpret_cast<unsigned long long*>(stats) + 4 * side : nullptr;
-    ea.T = seq_len;
+    ea.T = n_tokens;
+    ea.T_cap = capacity;
+    ea.t_off = t_off;
     ea.W = W;
     ea.n = n;
     ea.d = P.head_dim;
@@ -207,6 +225,163 @@ kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v
   return KVQ_OK;
 }
 
+// Decode attention of one query per sequence over n_tokens compressed tokens
+// (rows [0, n_tokens) of arrays holding `capacity` tokens per sequence) and
+// res_len uncompressed bf16 tokens (rows [0, res_len) of res_k / res_v, which
+// hold res_cap tokens per sequence).
+kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                          const uint8_t* k_cont, const uint8_t* v_cont, const uint16_t* k_so,
+                          const uint16_t* v_so, const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                          int64_t n_seqs, int64_t capacity, int64_t n_tokens, const void* res_k,
+                          const void* res_v, int64_t res_cap, int64_t res_len, float softmax_scale,
+                          void* out, float* out_f32, void* workspace, size_t workspace_bytes,
+                          void* hip_stream) {
+  if (!plan || !q || !out || !workspace) return KVQ_EINVAL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EINVAL;
+  if (out_f32 && !aligned16(out_f32)) return KVQ_EINVAL;
+  const kvq_params& P = plan->params;
+  const int Hkv = P.n_kv_heads, d = P.head_dim, W = P.mean_window;
+  if (n_q_heads < 1 || n_q_heads % Hkv) return KVQ_EINVAL;
+  if (n_seqs < 1 || n_tokens < 0 || n_tokens % W || res_len < 0 || n_tokens + res_len < 1)
+    return KVQ_EINVAL;
+  if (n_tokens > 0) {
+    if (!k_cont || !v_cont || !k_so || !v_so || !k_mean_q || !k_mean_scale) return KVQ_EINVAL;
+    const void* ptrs[] = {k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return KVQ_EINVAL;
+    if (capacity < n_tokens || capacity % W) return KVQ_EINVAL;
+  }
+  if (res_len > 0) {
+    if (!res_k || !res_v || !aligned16(res_k) || !aligned16(res_v) || res_cap < res_len) return KVQ_EINVAL;
+  }
+  const int G = n_q_heads / Hkv;
+  if (n_tokens % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W))
+    return KVQ_EUNSUPPORTED;
+  if (n_seqs > 65535) return KVQ_EUNSUPPORTED;
+  // the attention kernel addresses one sequence's containers with 32-bit offsets
+  if (int64_t(n_tokens) * std::max(P.container_bytes_k, P.container_bytes_v) + 16 > INT32_MAX)
+    return KVQ_EUNSUPPORTED;
+  const WsLayout wl = ws_layout(plan, n_seqs, n_tokens, n_q_heads);
+  if (workspace_bytes < wl.total) return KVQ_EWORKSPACE;
+  int nsplit;
+  int64_t tps;
+  split_geometry(n_seqs, n_tokens, &nsplit, &tps);
+  const int part_splits = nsplit + (res_len > 0 ? 1 : 0);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* qscale = reinterpret_cast<float*>(ws + wl.qscale);
+  float* qsum = reinterpret_cast<float*>(ws + wl.qsum);
+  float* qmu = reinterpret_cast<float*>(ws + wl.qmu);
+  float* part = reinterpret_cast<float*>(ws + wl.part);
+  const float tau = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
+
+  if (n_tokens > 0) {
+    kvq::Prologue2Args pa;
+    pa.q = static_cast<const uint16_t*>(q);
+    pa.mean_q = k_mean_q;
+    pa.mean_scale = k_mean_scale;
+    pa.qop = reinterpret_cast<uint16_t*>(ws + wl.qop);
+    pa.qscale = qscale;
+    pa.qsum = qsum;
+    pa.qmu = qmu;
+    pa.nW = n_tokens / W;
+    pa.nW_cap = capacity / W;
+    pa.Hq = n_q_heads;
+    pa.G = G;
+    pa.n = plan->n;
+    pa.hscale = plan->hadamard_scale;
+    if (kvq::launch_prologue2(pa, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
+
+    kvq::Attn2Args aa;
+    std::memset(&aa, 0, sizeof(aa));
+    aa.k_cont = k_cont;
+    aa.v_cont = v_cont;
+    aa.k_so = k_so;
+    aa.v_so = v_so;
+    aa.qop = reinterpret_cast<const uint4*>(ws + wl.qop);
+    aa.qscale = qscale;
+    aa.qsum = qsum;
+    aa.qmu = qmu;
+    aa.part = part;
+    aa.T = n_tokens;
+    aa.T_cap = capacity;
+    aa.tokens_per_split = tps;
+    aa.nW = n_tokens / W;
+    aa.nsplit = nsplit;
+    aa.part_splits = part_splits;
+    aa.log2W = 0;
+    while ((1 << aa.log2W) < W) ++aa.log2W;
+    aa.CK = P.container_bytes_k;
+    aa.CV = P.container_bytes_v;
+    aa.tau = tau;
+    aa.Mk = P.levels_k;
+    aa.Mv = P.levels_v;
+    for (int m = 0; m < kvq::kMaxLevels; ++m) {
+      aa.fk[m] = plan->side[0].freq[m];
+      aa.ck[m] = plan->side[0].cum[m];
+      aa.hbk[m] = plan->side[0].fp16_hi[m];
+      aa.fv[m] = plan->side[1].freq[m];
+      aa.cv[m] = plan->side[1].cum[m];
+      aa.hbv[m] = plan->side[1].fp16_hi[m];
+    }
+    size_t slot = 0;
+    const bool timed = timer_begin(stream, &slot);
+    if (kvq::launch_attention2(aa, n_seqs, n_q_heads, G, stream) != hipSuccess) return KVQ_EDEVICE;
+    if (timed) timer_end(stream, slot);
+  }
+  if (res_len > 0) {
+    kvq::ResidualArgs ra;
+    ra.q = static_cast<const uint16_t*>(q);
+    ra.k = static_cast<const uint16_t*>(res_k);
+    ra.v = static_cast<const uint16_t*>(res_v);
+    ra.part = part;
+    ra.R = res_len;
+    ra.R_cap = res_cap;
+    ra.nsplit_total = part_splits;
+    ra.split = nsplit;
+    ra.Hq = n_q_heads;
+    ra.G = G;
+    ra.d = d;
+    ra.tau = tau;
+    ra.hscale = plan->hadamard_scale;
+    if (kvq::launch_residual(ra, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
+  }
+
+  kvq::CombineArgs ca;
+  ca.part = part;
+  ca.out = static_cast<uint16_t*>(out);
+  ca.out_f32 = out_f32;
+  ca.nsplit = part_splits;
+  ca.Hq = n_q_heads;
+  ca.d = d;
+  ca.hscale = plan->hadamard_scale;
+  if (kvq::launch_combine(ca, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v,
+                              kvq_dtype in_dtype, int64_t n_seqs, int64_t seq_len,
+                              uint8_t* k_cont, uint8_t* v_cont, uint16_t* k_so, uint16_t* v_so,
+                              int8_t* k_mean_q, uint16_t* k_mean_scale, uint64_t* stats,
+                              void* hip_stream) {
+  return encode_impl(plan, k, v, in_dtype, n_seqs, seq_len, seq_len, 0, k_cont, v_cont, k_so, v_so,
+                     k_mean_q, k_mean_scale, stats, hip_stream);
+}
+
+kvq_status kvq_encode_append(const kvq_plan* plan, const void* k, const void* v,
+                             kvq_dtype in_dtype, int64_t n_seqs, int64_t n_tokens,
+                             int64_t cache_capacity, int64_t token_offset,
+                             uint8_t* k_cont, uint8_t* v_cont, uint16_t* k_so, uint16_t* v_so,
+                             int8_t* k_mean_q, uint16_t* k_mean_scale, uint64_t* stats,
+                             void* hip_stream) {
+  return encode_impl(plan, k, v, in_dtype, n_seqs, n_tokens, cache_capacity, token_offset, k_cont,
+                     v_cont, k_so, v_so, k_mean_q, k_mean_scale, stats, hip_stream);
+}
+
 kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q_heads,
                                 const uint8_t* k_cont, const uint8_t* v_cont,
                                 const uint16_t* k_so, const uint16_t* v_so,
@@ -214,96 +389,23 @@ kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q
                                 int64_t n_seqs, int64_t seq_len, float softmax_scale,
                                 void* out, float* out_f32, void* workspace,
                                 size_t workspace_bytes, void* hip_stream) {
-  if (!plan || !q || !k_cont || !v_cont || !k_so || !v_so || !k_mean_q || !k_mean_scale || !out ||
-      !workspace)
-    return KVQ_EINVAL;
-  const void* ptrs[] = {q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, out, workspace};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return KVQ_EINVAL;
-  if (out_f32 && !aligned16(out_f32)) return KVQ_EINVAL;
-  const kvq_params& P = plan->params;
-  const int Hkv = P.n_kv_heads, d = P.head_dim, W = P.mean_window;
-  if (n_q_heads < 1 || n_q_heads % Hkv) return KVQ_EINVAL;
-  if (n_seqs < 1 || seq_len < W || seq_len % W) return KVQ_EINVAL;
-  const int G = n_q_heads / Hkv;
-  if (seq_len % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W))
-    return KVQ_EUNSUPPORTED;
-  if (n_seqs > 65535) return KVQ_EUNSUPPORTED;
-  // the attention kernel addresses one sequence's containers with 32-bit offsets
-  if (int64_t(seq_len) * std::max(P.container_bytes_k, P.container_bytes_v) + 16 > INT32_MAX)
-    return KVQ_EUNSUPPORTED;
-  const WsLayout wl = ws_layout(plan, n_seqs, seq_len, n_q_heads);
-  if (workspace_bytes < wl.total) return KVQ_EWORKSPACE;
-  int nsplit;
-  int64_t tps;
-  split_geometry(n_seqs, seq_len, &nsplit, &tps);
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* qscale = reinterpret_cast<float*>(ws + wl.qscale);
-  float* qsum = reinterpret_cast<float*>(ws + wl.qsum);
-  float* qmu = reinterpret_cast<float*>(ws + wl.qmu);
-  float* part = reinterpret_cast<float*>(ws + wl.part);
+  if (seq_len < 1) return KVQ_EINVAL;
+  return attention_impl(plan, q, n_q_heads, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, n_seqs,
+                        seq_len, seq_len, nullptr, nullptr, 0, 0, softmax_scale, out, out_f32, workspace,
+                        workspace_bytes, hip_stream);
+}
 
-  kvq::Prologue2Args pa;
-  pa.q = static_cast<const uint16_t*>(q);
-  pa.mean_q = k_mean_q;
-  pa.mean_scale = k_mean_scale;
-  pa.qop = reinterpret_cast<uint16_t*>(ws + wl.qop);
-  pa.qscale = qscale;
-  pa.qsum = qsum;
-  pa.qmu = qmu;
-  pa.nW = seq_len / W;
-  pa.Hq = n_q_heads;
-  pa.G = G;
-  pa.n = plan->n;
-  pa.hscale = plan->hadamard_scale;
-  if (kvq::launch_prologue2(pa, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
-
-  kvq::Attn2Args aa;
-  std::memset(&aa, 0, sizeof(aa));
-  aa.k_cont = k_cont;
-  aa.v_cont = v_cont;
-  aa.k_so = k_so;
-  aa.v_so = v_so;
-  aa.qop = reinterpret_cast<const uint4*>(ws + wl.qop);
-  aa.qscale = qscale;
-  aa.qsum = qsum;
-  aa.qmu = qmu;
-  aa.part = part;
-  aa.T = seq_len;
-  aa.tokens_per_split = tps;
-  aa.nW = seq_len / W;
-  aa.nsplit = nsplit;
-  aa.log2W = 0;
-  while ((1 << aa.log2W) < W) ++aa.log2W;
-  aa.CK = P.container_bytes_k;
-  aa.CV = P.container_bytes_v;
-  aa.tau = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(d)));
-  aa.Mk = P.levels_k;
-  aa.Mv = P.levels_v;
-  for (int m = 0; m < kvq::kMaxLevels; ++m) {
-    aa.fk[m] = plan->side[0].freq[m];
-    aa.ck[m] = plan->side[0].cum[m];
-    aa.hbk[m] = plan->side[0].fp16_hi[m];
-    aa.fv[m] = plan->side[1].freq[m];
-    aa.cv[m] = plan->side[1].cum[m];
-    aa.hbv[m] = plan->side[1].fp16_hi[m];
-  }
-  size_t slot = 0;
-  const bool timed = timer_begin(stream, &slot);
-  if (kvq::launch_attention2(aa, n_seqs, n_q_heads, G, stream) != hipSuccess) return KVQ_EDEVICE;
-  if (timed) timer_end(stream, slot);
-
-  kvq::CombineArgs ca;
-  ca.part = part;
-  ca.out = static_cast<uint16_t*>(out);
-  ca.out_f32 = out_f32;
-  ca.nsplit = nsplit;
-  ca.Hq = n_q_heads;
-  ca.d = d;
-  ca.hscale = plan->hadamard_scale;
-  if (kvq::launch_combine(ca, n_seqs, stream) != hipSuccess) return KVQ_EDEVICE;
-  return KVQ_OK;
+kvq_status kvq_decode_attention_ex(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                                   const uint8_t* k_cont, const uint8_t* v_cont,
+                                   const uint16_t* k_so, const uint16_t* v_so,
+                                   const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                                   int64_t n_seqs, int64_t cache_capacity, int64_t n_tokens,
+                                   const void* res_k, const void* res_v, int64_t res_capacity,
+                                   int64_t res_len, float softmax_scale, void* out, float* out_f32,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return attention_impl(plan, q, n_q_heads, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, n_seqs,
+                        cache_capacity, n_tokens, res_k, res_v, res_capacity, res_len, softmax_scale, out,
+                        out_f32, workspace, workspace_bytes, hip_stream);
 }
 
 kvq_status kvq_decode_symbols(const kvq_plan* plan, int side, const uint8_t* cont,

@@ -220,8 +220,8 @@ __global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
     a.qscale[s * a.Hq + h] = ldexpf(1.0f, -e);
   }
   for (int64_t w = 0; w < a.nW; ++w) {
-    const float sc = h2f(a.mean_scale[s * a.nW + w]);
-    const int8_t* mq = a.mean_q + (s * a.nW + w) * a.n + int64_t(g) * kD + lane * 2;
+    const float sc = h2f(a.mean_scale[s * a.nW_cap + w]);
+    const int8_t* mq = a.mean_q + (s * a.nW_cap + w) * a.n + int64_t(g) * kD + lane * 2;
     float acc = q[0] * __fmul_rn(float(mq[0]), sc) + q[1] * __fmul_rn(float(mq[1]), sc);
     acc = wave_sum_f(acc);
     if (lane == 0) a.qmu[(s * a.Hq + h) * a.nW + w] = acc;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64, 2) void attention2_kernel(Attn2Args a) {
   const int qn = lane & 3;   // A-operand row = query slot within a group of 4
 
   for (int64_t t0 = tb; t0 < te; t0 += 64) {
-    const int64_t row = s * a.T + t0 + lane;
+    const int64_t row = s * a.T_cap + t0 + lane;
     const float sk = h2f(a.k_so[2 * row]), ok = h2f(a.k_so[2 * row + 1]);
     // the 64-token tile lies in one key-mean window (W >= 64, tiles aligned)
     const int64_t w = t0 >> a.log2W;
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(64, 2) void attention2_kernel(Attn2Args a) {
   }
 
   // partials: lane holds channel c*64 + lane of every query head
-  float* P = a.part + (s * a.nsplit + split) * int64_t(HQ) * (kD + 4);
+  float* P = a.part + (s * a.part_splits + split) * int64_t(HQ) * (kD + 4);
 #pragma unroll
   for (int g = 0; g < HKV; ++g)
 #pragma unroll
@@ -680,8 +680,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   uint32_t xk = 0, xv = 0;
   float sk = 0.f, ok = 0.f, svK = 0.f, ovK = 0.f;
   // buffer resources over this sequence's containers (T C < 2^31, checked by the host)
-  const uint8_t* const kseq = a.k_cont + s * a.T * a.CK;
-  const uint8_t* const vseq = a.v_cont + s * a.T * a.CV;
+  const uint8_t* const kseq = a.k_cont + s * a.T_cap * a.CK;
+  const uint8_t* const vseq = a.v_cont + s * a.T_cap * a.CV;
   const __amdgpu_buffer_rsrc_t rsK = seq_rsrc(kseq, uint32_t(a.T * a.CK));
   const __amdgpu_buffer_rsrc_t rsV = seq_rsrc(vseq, uint32_t(a.T * a.CV));
   const uint32_t misK = uint32_t(reinterpret_cast<uintptr_t>(kseq) & 15u);
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
       if (!kreal && g > 0) break;
       // ---- stream starts
       if (g == 0) {
-        const int64_t row = s * a.T + tK + lane;
+        const int64_t row = s * a.T_cap + tK + lane;
         xk = ring5_start(rk, lds, rsK, misK + uint32_t(tK + lane) * uint32_t(a.CK), uint32_t(a.CK));
         sk = h2f(a.k_so[2 * row]);
         ok = h2f(a.k_so[2 * row + 1]);
@@ -818,7 +818,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
     }
   }
 
-  float* P = a.part + (s * a.nsplit + split) * int64_t(HQ) * (kD + 4);
+  float* P = a.part + (s * a.part_splits + split) * int64_t(HQ) * (kD + 4);
 #pragma unroll
   for (int g = 0; g < HKV; ++g)
 #pragma unroll

@@ -88,6 +88,103 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- residual
+// The most recent tokens of every sequence kept uncompressed in bf16
+// ([D-Quant] §5.1 "Implementation details") join the same softmax as one more
+// split of partials.  One wave per (KV head, sequence): per 64-token chunk,
+// lane t computes the logits of token t for the G query heads, the chunk's
+// max / sum update the running softmax state, and lane j then accumulates
+// channels 2j, 2j+1 of sum_t p_t v_t.  The accumulator is rotated (orthonormal
+// Hadamard, its own inverse) so that it matches the rotated partials of the
+// compressed splits; the offset sum Z is zero.
+constexpr int kResMaxG = 8;
+
+__global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x;
+  const int64_t s = blockIdx.y;
+  const int G = a.G, d = a.d;                 // d == 128: two channels per lane
+  const int hkv = a.Hq / G;
+  __shared__ float qs[kResMaxG][128];
+  __shared__ float ps[kResMaxG][64];
+  for (int i = lane; i < G * d; i += 64) {
+    const int h = i / d, j = i % d;
+    qs[h][j] = bf16_bits_to_f32(a.q[(s * a.Hq + g * G + h) * d + j]);
+  }
+  __syncthreads();
+  float M[kResMaxG], L[kResMaxG], acc[kResMaxG][2];
+#pragma unroll
+  for (int h = 0; h < kResMaxG; ++h) {
+    M[h] = -__builtin_inff();
+    L[h] = 0.f;
+    acc[h][0] = acc[h][1] = 0.f;
+  }
+  const int64_t row_stride = int64_t(hkv) * d;          // elements per token
+  const uint16_t* kb = a.k + (s * a.R_cap) * row_stride + int64_t(g) * d;
+  const uint16_t* vb = a.v + (s * a.R_cap) * row_stride + int64_t(g) * d;
+  for (int64_t t0 = 0; t0 < a.R; t0 += 64) {
+    const int64_t t = t0 + lane;
+    const bool live = t < a.R;
+    float lg[kResMaxG];
+#pragma unroll
+    for (int h = 0; h < kResMaxG; ++h) lg[h] = 0.f;
+    if (live) {
+      const uint16_t* kr = kb + t * row_stride;
+      for (int j = 0; j < d; j += 2) {
+        const uint32_t two = *reinterpret_cast<const uint32_t*>(kr + j);
+        const float k0 = __uint_as_float(two << 16), k1 = __uint_as_float(two & 0xFFFF0000u);
+#pragma unroll
+        for (int h = 0; h < kResMaxG; ++h)
+          if (h < G) lg[h] += qs[h][j] * k0 + qs[h][j + 1] * k1;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < kResMaxG; ++h) {
+      if (h < G) {
+        const float l = live ? lg[h] * a.tau : -__builtin_inff();
+        const float mx = fmaxf(M[h], wave_max(l));
+        const float al = __expf(M[h] - mx);             // 0 on the first chunk
+        const float p = live ? __expf(l - mx) : 0.f;
+        L[h] = L[h] * al + wave_sum_f32(p);
+        M[h] = mx;
+        acc[h][0] *= al;
+        acc[h][1] *= al;
+        ps[h][lane] = p;
+      }
+    }
+    __syncthreads();
+    const int64_t tn = a.R - t0 < 64 ? a.R - t0 : 64;
+    for (int64_t u = 0; u < tn; ++u) {
+      const uint32_t two = *reinterpret_cast<const uint32_t*>(vb + (t0 + u) * row_stride + 2 * lane);
+      const float v0 = __uint_as_float(two << 16), v1 = __uint_as_float(two & 0xFFFF0000u);
+#pragma unroll
+      for (int h = 0; h < kResMaxG; ++h)
+        if (h < G) {
+          acc[h][0] += ps[h][u] * v0;
+          acc[h][1] += ps[h][u] * v1;
+        }
+    }
+    __syncthreads();
+  }
+  const int stride = d + 4;
+#pragma unroll
+  for (int h = 0; h < kResMaxG; ++h) {
+    if (h < G) {
+      float o[2] = {acc[h][0], acc[h][1]};
+      fwht_lanes<2>(o, d, lane, a.hscale);
+      float* P = a.part + ((s * a.nsplit_total + a.split) * a.Hq + g * G + h) * int64_t(stride);
+      P[2 * lane] = o[0];
+      P[2 * lane + 1] = o[1];
+      if (lane == 0) {
+        P[d] = M[h];
+        P[d + 1] = L[h];
+        P[d + 2] = 0.f;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_symbols(const DecSymArgs& a, hipStream_t stream) {
@@ -104,6 +201,12 @@ hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream) {
     case 256: hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(64), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_residual(const ResidualArgs& a, int64_t S, hipStream_t stream) {
+  if (a.d != 128 || a.G < 1 || a.G > kResMaxG) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(residual_kernel, dim3(unsigned(a.Hq / a.G), unsigned(S)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -11,11 +11,13 @@ namespace kvq {
 
 // ----------------------------------------------------------------- encoder
 struct KeyMeanArgs {
-  const void* k;
+  const void* k;              // [S, T, n] (the tokens being encoded)
   int in_bf16;
-  int8_t* mean_q;
-  uint16_t* mean_scale;
-  int64_t T;
+  int8_t* mean_q;             // [S, T_cap / W, n]
+  uint16_t* mean_scale;       // [S, T_cap / W]
+  int64_t T;                  // tokens per sequence in k
+  int64_t T_cap;              // tokens per sequence in the cache arrays
+  int64_t t_off;              // cache position of k's first token (multiple of W)
   int W, n, d;
   float hscale;
 };
@@ -34,15 +36,17 @@ struct EncTabs {
 };
 
 struct EncodeArgs {
-  const void* x;
+  const void* x;               // [S, T, n]
   int in_bf16;
   int is_key;
-  const int8_t* mean_q;
-  const uint16_t* mean_scale;
-  uint8_t* cont;
-  uint16_t* so;
+  const int8_t* mean_q;        // [S, T_cap / W, n]
+  const uint16_t* mean_scale;  // [S, T_cap / W]
+  uint8_t* cont;               // [S, T_cap, C]
+  uint16_t* so;                // [S, T_cap, 2]
   unsigned long long* stats;   // already offset to the side's 4 counters
-  int64_t T;
+  int64_t T;                   // tokens per sequence in x (a multiple of spw)
+  int64_t T_cap;               // tokens per sequence in the cache arrays
+  int64_t t_off;               // cache position of x's first token
   int W, n, d;
   float hscale;
   int spw;                     // streams per workgroup (multiple of 4)
@@ -79,7 +83,8 @@ struct Prologue2Args {
   float* qscale;              // [S, Hq]: 2^-e undoing the operand scaling
   float* qsum;                // [S, Hq]
   float* qmu;                 // [S, Hq, nW]
-  int64_t nW;
+  int64_t nW;                 // windows attended per sequence
+  int64_t nW_cap;             // windows per sequence in the mean arrays
   int Hq, G, n;
   float hscale;
 };
@@ -93,15 +98,29 @@ struct Attn2Args {
   const float* qscale;
   const float* qsum;
   const float* qmu;
-  float* part;                // [S, nsplit, Hq, 128 + 4]
-  int64_t T;
+  float* part;                // [S, nsplit (+1 residual), Hq, 128 + 4]
+  int64_t T;                  // tokens attended per sequence
+  int64_t T_cap;              // tokens per sequence in the cache arrays
   int64_t tokens_per_split;
   int64_t nW;
   int nsplit, log2W, CK, CV;
+  int part_splits;             // splits per sequence in `part` (nsplit, +1 with a residual)
   float tau;
   int Mk, Mv;
   uint32_t fk[kMaxLevels], ck[kMaxLevels], hbk[kMaxLevels];
   uint32_t fv[kMaxLevels], cv[kMaxLevels], hbv[kMaxLevels];
+};
+
+// The uncompressed tail of every sequence (the most recent tokens, kept in
+// bf16) as one more split of partials.
+struct ResidualArgs {
+  const uint16_t* q;          // bf16 [S, Hq, d]
+  const uint16_t* k;          // bf16 [S, R_cap, Hkv, d]
+  const uint16_t* v;
+  float* part;                // [S, nsplit_total, Hq, d + 4]; this writes split `split`
+  int64_t R, R_cap;
+  int nsplit_total, split, Hq, G, d;
+  float tau, hscale;
 };
 
 struct CombineArgs {
@@ -219,6 +238,7 @@ hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t strea
 hipError_t launch_attention2(const Attn2Args& a, int64_t S, int Hq, int G, hipStream_t stream);
 bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int window);
 hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream);
+hipError_t launch_residual(const ResidualArgs& a, int64_t S, hipStream_t stream);
 
 }  // namespace kvq
 

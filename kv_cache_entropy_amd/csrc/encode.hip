@@ -74,7 +74,7 @@ __global__ __launch_bounds__(1024) void key_mean_kernel(KeyMeanArgs a) {
     }
     packed |= (uint32_t(qv) & 0xFFu) << (8 * i);
   }
-  const int64_t orow = (seq * nW + win);
+  const int64_t orow = seq * (a.T_cap / a.W) + a.t_off / a.W + win;
   if (active) *reinterpret_cast<uint32_t*>(a.mean_q + orow * a.n + j0) = packed;
   if (tid == 0) a.mean_scale[orow] = __half_as_ushort(sc16);
 }
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     fwht_lanes<NPL>(x, a.d, lane, a.hscale);
     if (a.is_key) {
       const int64_t seq = st / a.T, t = st % a.T;
-      const int64_t row = seq * (a.T / a.W) + t / a.W;
+      const int64_t row = seq * (a.T_cap / a.W) + (a.t_off + t) / a.W;
       const float sc = __half2float(__ushort_as_half(a.mean_scale[row]));
       const int8_t* mq = a.mean_q + row * n + int64_t(lane) * NPL;
 #pragma unroll
@@ -310,15 +310,20 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     if (lane == 0) so_sh[sl] = uint32_t(__half_as_ushort(s16)) | (uint32_t(__half_as_ushort(o16)) << 16);
   }
   __syncthreads();
+  // the SPW streams lie in one sequence (T is a multiple of SPW): their cache
+  // rows are contiguous from ost0
+  const int64_t seq0 = stream0 / a.T;
+  const int64_t ost0 = seq0 * a.T_cap + a.t_off + (stream0 - seq0 * a.T);
   uint32_t overrun = 0;
   if (tid < SPW) {
     overrun = rans_encode_lane(sym + size_t(tid) * n, n, img + size_t(tid) * C, C, sh) ? 0u : 1u;
-    reinterpret_cast<uint32_t*>(a.so)[stream0 + tid] = so_sh[tid];
+    reinterpret_cast<uint32_t*>(a.so)[ost0 + tid] = so_sh[tid];
   }
   __syncthreads();
-  // SPW * C is a multiple of 4 (SPW is a multiple of 4); the base is 16-aligned
+  // SPW * C is a multiple of 4 (SPW is a multiple of 4); ost0 * C is a multiple of 4
+  // because ost0 is a multiple of SPW
   const int nwords = SPW * C / 4;
-  uint32_t* gdst = reinterpret_cast<uint32_t*>(a.cont + stream0 * C);
+  uint32_t* gdst = reinterpret_cast<uint32_t*>(a.cont + ost0 * C);
   const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(img);
   for (int i = tid; i < nwords; i += 256) gdst[i] = ssrc[i];
   if (a.stats) {

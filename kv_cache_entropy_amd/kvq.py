@@ -48,6 +48,10 @@ _SIGS = {
     "kvq_encode_streams": (_I32, [_P, _P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kvq_decode_attention": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float,
                                     _P, _P, _P, ctypes.c_size_t, _P]),
+    "kvq_encode_append": (_I32, [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P,
+                                 _P, _P, _P]),
+    "kvq_decode_attention_ex": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P,
+                                       _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "kvq_decode_symbols": (_I32, [_P, ctypes.c_int, _P, _I64, _P, _P, _P]),
     "kvq_status_str": (ctypes.c_char_p, [_I32]),
     "kvq_timing_enable": (_I32, [ctypes.c_int]),
@@ -169,6 +173,42 @@ def kvq_decode_attention(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_s
         plan.handle, _ptr(q), Hq, _ptr(k_cont), _ptr(v_cont), _ptr(k_so), _ptr(v_so),
         _ptr(k_mean_q), _ptr(k_mean_scale), S, T, float(softmax_scale), _ptr(out), _ptr(out_f32),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def kvq_encode_append(plan, k, v, cache, token_offset, stats=None, stream=None):
+    """Encodes k, v [S, T', Hkv, d] into rows [token_offset, token_offset + T') of `cache`
+    (the dict of alloc_cache, whose second dimension is the capacity)."""
+    if k.dtype != v.dtype or k.shape != v.shape:
+        raise ValueError("k and v must have the same dtype and shape")
+    dt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}.get(k.dtype)
+    if dt is None:
+        raise TypeError("k/v must be float32 or bfloat16")
+    S, T = int(k.shape[0]), int(k.shape[1])
+    cap = int(cache["k_cont"].shape[1])
+    _check("kvq_encode_append", lib().kvq_encode_append(
+        plan.handle, _ptr(k), _ptr(v), dt, S, T, cap, int(token_offset), _ptr(cache["k_cont"]),
+        _ptr(cache["v_cont"]), _ptr(cache["k_so"]), _ptr(cache["v_so"]), _ptr(cache["k_mean_q"]),
+        _ptr(cache["k_mean_scale"]), _ptr(stats), _stream(stream)))
+
+
+def kvq_decode_attention_ex(plan, q, cache, n_tokens, res_k, res_v, res_len, out, workspace,
+                            out_f32=None, softmax_scale=0.0, stream=None):
+    """Attention over rows [0, n_tokens) of `cache` (capacity = its second dimension;
+    may be None when n_tokens == 0) and rows [0, res_len) of res_k / res_v
+    [S, R_cap, Hkv, d] bf16 (may be None when res_len == 0)."""
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("q and out must be bfloat16")
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    c = cache or {}
+    cap = int(c["k_cont"].shape[1]) if cache is not None else 0
+    rcap = int(res_k.shape[1]) if res_k is not None else 0
+    if res_k is not None and (res_k.dtype != torch.bfloat16 or res_v.dtype != torch.bfloat16):
+        raise TypeError("res_k and res_v must be bfloat16")
+    _check("kvq_decode_attention_ex", lib().kvq_decode_attention_ex(
+        plan.handle, _ptr(q), Hq, _ptr(c.get("k_cont")), _ptr(c.get("v_cont")), _ptr(c.get("k_so")),
+        _ptr(c.get("v_so")), _ptr(c.get("k_mean_q")), _ptr(c.get("k_mean_scale")), S, cap,
+        int(n_tokens), _ptr(res_k), _ptr(res_v), rcap, int(res_len), float(softmax_scale), _ptr(out),
+        _ptr(out_f32), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def kvq_decode_symbols(plan, side, cont, symbols, end_ok=None, stream=None):

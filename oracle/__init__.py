@@ -41,7 +41,7 @@ from .quant import (fit_minmax, drift, refit, refit_f64, lane_sum_f64,
                     nearest_levels, encode_streams_alg1)
 from .rans import rans_encode, rans_decode
 from .attention import (dequantize_f64, attention_plain_f64,
-                        attention_factored_f64)
+                        attention_factored_f64, attention_with_residual_f64)
 from .accounting import bits_per_elem, containers_for_budget
 from .pipeline import OracleParams, encode_cache, decode_cache_symbols
 
@@ -52,6 +52,6 @@ __all__ = [
     "decode_table", "fwht_f32", "hadamard_f64", "rotate_heads",
     "key_window_mean", "fit_minmax", "drift", "refit", "encode_streams_alg1",
     "rans_encode", "rans_decode", "dequantize_f64", "attention_plain_f64",
-    "attention_factored_f64", "bits_per_elem", "containers_for_budget",
+    "attention_factored_f64", "attention_with_residual_f64", "bits_per_elem", "containers_for_budget",
     "OracleParams", "encode_cache", "decode_cache_symbols",
 ]

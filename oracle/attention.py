@@ -12,7 +12,9 @@ G = Hq / Hkv.
 
 ``attention_plain_f64`` is the plain definition: dequantise, rotate back,
 softmax(q K^T tau) V.  ``attention_factored_f64`` evaluates Eqs. (8)-(9) and is
-checked against it.
+checked against it.  ``attention_with_residual_f64`` adds the most recent
+tokens kept uncompressed ([D-Quant] §5.1 "Implementation details": the latest
+tokens stay in BF16): they join the same softmax with their raw values.
 """
 
 import numpy as np
@@ -78,4 +80,31 @@ def attention_factored_f64(q, k_sym, k_so16, mu_hat_tok, v_sym, v_so16,
         a = _softmax_rows(logit)
         o_rot = (a * vs[:, 0]) @ vm[:, g, :] + (a * vs[:, 1]).sum()
         out[h] = H @ o_rot
+    return out
+
+
+def attention_with_residual_f64(q, khat_rot, vhat_rot, res_k, res_v, n_kv_heads, head_dim,
+                                scale=None):
+    """Plain attention over T compressed tokens (khat_rot, vhat_rot [T, n] in
+    the rotated basis, T may be 0) followed by R uncompressed tokens (res_k,
+    res_v [R, n] in the original basis, R may be 0)."""
+    q = np.asarray(q, F64)
+    Hq, d = q.shape
+    G = Hq // n_kv_heads
+    tau = 1.0 / np.sqrt(float(d)) if scale is None else float(scale)
+    H = hadamard_f64(d)
+    n = n_kv_heads * head_dim
+    kr = np.asarray(khat_rot, F64).reshape(-1, n)
+    vr = np.asarray(vhat_rot, F64).reshape(-1, n)
+    K = np.concatenate([(kr.reshape(-1, n_kv_heads, d) @ H),
+                        np.asarray(res_k, F64).reshape(-1, n_kv_heads, d)])
+    V = np.concatenate([(vr.reshape(-1, n_kv_heads, d) @ H),
+                        np.asarray(res_v, F64).reshape(-1, n_kv_heads, d)])
+    if K.shape[0] == 0:
+        raise ValueError("attention over zero tokens")
+    out = np.zeros((Hq, d), F64)
+    for h in range(Hq):
+        g = h // G
+        a = _softmax_rows((K[:, g, :] @ q[h]) * tau)
+        out[h] = a @ V[:, g, :]
     return out

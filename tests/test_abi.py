@@ -98,3 +98,30 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
                                   a16, None, a16, 1 << 30, st) == -3
     assert L.kvq_decode_symbols(plan.handle, 2, a16, 4, a16, None, st) == -1
     assert plan.workspace_bytes(0, 4, 1024, 32) == 0
+
+
+def test_append_and_residual_entry_points_reject_bad_arguments():
+    L = _lib()
+    plan = kvq.Plan(8, 128)
+    p = ctypes.c_void_p
+    a16 = p(1 << 20)                          # never dereferenced: checks fail first
+    st = p(0)
+    ok_args = lambda **kw: dict(dict(n=128, cap=1024, off=0), **kw)
+
+    def append(n, cap, off):
+        return L.kvq_encode_append(plan.handle, a16, a16, 1, 2, n, cap, off, a16, a16, a16, a16, a16,
+                                   a16, None, st)
+    assert append(**ok_args(off=64)) == -1            # offset not a multiple of W
+    assert append(**ok_args(n=100)) == -1             # tokens not a multiple of W
+    assert append(**ok_args(off=1024)) == -1          # past the capacity
+    assert append(**ok_args(cap=1000)) == -1          # capacity not a multiple of W
+
+    def attend(n_tok, res_len, res_cap=256, res=a16, cap=1024):
+        return L.kvq_decode_attention_ex(plan.handle, a16, 32, a16, a16, a16, a16, a16, a16, 2, cap, n_tok,
+                                         res, res, res_cap, res_len, 0.0, a16, None, a16, 1 << 30, st)
+    assert attend(0, 0) == -1                         # nothing to attend
+    assert attend(128, 300) == -1                     # tail longer than its buffer
+    assert attend(0, 10, res=None) == -1              # tail without buffers
+    assert attend(100, 0) == -1                       # not a multiple of W
+    assert attend(2048, 0) == -1                      # more tokens than the capacity
+    assert plan.workspace_bytes(1, 2, 0, 32) > 0      # a tail-only call still needs partials
