@@ -136,6 +136,14 @@ def main():
     base_k = [k[s, :base_tokens].float().cpu().numpy() for s in base_seqs]
     base_v = [v[s, :base_tokens].float().cpu().numpy() for s in base_seqs]
     base_q = [q[s].float().cpu().numpy() for s in base_seqs]
+    # the last key-mean window of every sequence, for the streaming measurements
+    W = 128
+    stream_ok = T >= 2 * W
+    if stream_ok:
+        win_k = k[:, T - W:].contiguous()
+        win_v = v[:, T - W:].contiguous()
+        win_k16 = win_k.to(torch.bfloat16)
+        win_v16 = win_v.to(torch.bfloat16)
     del k, v
     torch.cuda.empty_cache()
 
@@ -174,6 +182,43 @@ def main():
         f"({achieved:.1f} GB/s) over {klaunch} launches")
 
     traffic = measured_traffic(f"{w.name}@{ck}/{cv}", kernel_bytes)
+
+    # ---- streaming decode: a compressed prefix of T - W tokens plus a bf16 tail
+    # of W - 1 tokens, and the append of one W-token window per sequence
+    streaming = None
+    if stream_ok:
+        n_pre, r_len = T - W, W - 1
+        ws_ex = torch.empty(plan.workspace_bytes(1, S, n_pre, Hq), dtype=torch.uint8, device=dev)
+
+        def step_ex(i):
+            kvq.kvq_decode_attention_ex(plan, q, caches[i % copies], n_pre, win_k16, win_v16, r_len,
+                                        out, ws_ex)
+
+        for i in range(args.warmup):
+            step_ex(i)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            step_ex(i)
+        t1.record()
+        torch.cuda.synchronize()
+        ex_ms = t0.elapsed_time(t1) / args.steps
+        ex_bytes = S * n_pre * (ck + cv + 8) + S * (n_pre // W) * (n + 2) + S * r_len * n * 2 * 2
+        reps = 3
+        kvq.kvq_encode_append(plan, win_k, win_v, cache, T - W)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            kvq.kvq_encode_append(plan, win_k, win_v, cache, T - W)
+        t1.record()
+        torch.cuda.synchronize()
+        app_ms = t0.elapsed_time(t1) / reps
+        streaming = {"prefix_tokens": n_pre, "bf16_tail_tokens": r_len,
+                     "step_ms": round(ex_ms, 4), "step_gb_per_s": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 2),
+                     "append_window_ms": round(app_ms, 3),
+                     "append_token_layers_per_s": round(S * W / (app_ms * 1e-3), 1)}
+        log(f"[bench] streaming: prefix {n_pre} + bf16 tail {r_len}: {ex_ms:.3f} ms/step; "
+            f"append of one {W}-token window per sequence {app_ms:.3f} ms")
 
     # ---- CPU baseline: the oracle's read side on a bounded sample
     cpu = None
@@ -224,10 +269,11 @@ def main():
                         "v_changed": stats_once[6], "v_overruns": stats_once[7],
                         "symbols_per_side": S * T * n},
         "rotated_copies": copies,
+        "streaming": streaming,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "attention_kernel", "kernel_ms": round(kernel_ms, 4),
+                     "kernel": "attention4_kernel", "kernel_ms": round(kernel_ms, 4),
                      "algorithmic_bytes_per_launch": kernel_bytes},
         "cpu_baseline": cpu,
     }

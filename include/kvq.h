@@ -78,6 +78,12 @@ void kvq_plan_destroy(kvq_plan* plan);
 kvq_status kvq_plan_tables(const kvq_plan* plan, int side, uint16_t* freq,
                            uint16_t* cum, int32_t* rate_fx);
 
+/* The probability model itself ([D-Quant] §4.2, §4.4): expected fraction of
+ * each of `levels` symbols when n iid N(0,1) values are min-max normalised and
+ * rounded to the nearest level, raised to alpha and renormalised (alpha = 1:
+ * the plain model).  Writes `levels` doubles.  KVQ_EINVAL out of range. */
+kvq_status kvq_model_probs(int32_t levels, int32_t n, double alpha, double* probs);
+
 /* Copies the 512-entry lambda grid E[k] = fp32(2^(k/512)) to host memory. */
 kvq_status kvq_plan_lambda_grid(const kvq_plan* plan, float* grid512);
 

@@ -129,13 +129,22 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
 #pragma unroll
     for (int h = 0; h < kResMaxG; ++h) lg[h] = 0.f;
     if (live) {
-      const uint16_t* kr = kb + t * row_stride;
-      for (int j = 0; j < d; j += 2) {
-        const uint32_t two = *reinterpret_cast<const uint32_t*>(kr + j);
-        const float k0 = __uint_as_float(two << 16), k1 = __uint_as_float(two & 0xFFFF0000u);
+      // the token's 128 key values as 16 independent 16-byte loads
+      const uint4* kr = reinterpret_cast<const uint4*>(kb + t * row_stride);
+      uint4 kv[16];
 #pragma unroll
-        for (int h = 0; h < kResMaxG; ++h)
-          if (h < G) lg[h] += qs[h][j] * k0 + qs[h][j + 1] * k1;
+      for (int c = 0; c < 16; ++c) kv[c] = kr[c];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const uint32_t w4[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 8 * c + 2 * e;
+          const float k0 = __uint_as_float(w4[e] << 16), k1 = __uint_as_float(w4[e] & 0xFFFF0000u);
+#pragma unroll
+          for (int h = 0; h < kResMaxG; ++h)
+            if (h < G) lg[h] += qs[h][j] * k0 + qs[h][j + 1] * k1;
+        }
       }
     }
     __syncthreads();
@@ -154,16 +163,24 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
       }
     }
     __syncthreads();
-    const int64_t tn = a.R - t0 < 64 ? a.R - t0 : 64;
-    for (int64_t u = 0; u < tn; ++u) {
-      const uint32_t two = *reinterpret_cast<const uint32_t*>(vb + (t0 + u) * row_stride + 2 * lane);
-      const float v0 = __uint_as_float(two << 16), v1 = __uint_as_float(two & 0xFFFF0000u);
+    const int tn = int(a.R - t0 < 64 ? a.R - t0 : 64);
+    for (int u0 = 0; u0 < tn; u0 += 8) {
+      // 8 value rows in flight (rows past the tail are not loaded)
+      uint32_t two[8];
 #pragma unroll
-      for (int h = 0; h < kResMaxG; ++h)
-        if (h < G) {
-          acc[h][0] += ps[h][u] * v0;
-          acc[h][1] += ps[h][u] * v1;
-        }
+      for (int e = 0; e < 8; ++e)
+        two[e] = u0 + e < tn ? *reinterpret_cast<const uint32_t*>(vb + (t0 + u0 + e) * row_stride + 2 * lane)
+                             : 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v0 = __uint_as_float(two[e] << 16), v1 = __uint_as_float(two[e] & 0xFFFF0000u);
+#pragma unroll
+        for (int h = 0; h < kResMaxG; ++h)
+          if (h < G && u0 + e < tn) {
+            acc[h][0] += ps[h][u0 + e] * v0;
+            acc[h][1] += ps[h][u0 + e] * v1;
+          }
+      }
     }
     __syncthreads();
   }

@@ -253,6 +253,16 @@ kvq_status kvq_plan_lambda_grid(const kvq_plan* plan, float* grid512) {
   return KVQ_OK;
 }
 
+kvq_status kvq_model_probs(int32_t levels, int32_t n, double alpha, double* probs) {
+  if (!probs || levels < 2 || levels > kvq::kMaxLevels || n < 2 || n > 4096) return KVQ_EINVAL;
+  if (!(alpha >= 1.0) || !(alpha <= 16.0)) return KVQ_EINVAL;
+  const std::vector<double> p = order_stat_probs(levels, n);
+  double tot = 0.0;
+  for (int m = 0; m < levels; ++m) tot += std::pow(p[m], alpha);
+  for (int m = 0; m < levels; ++m) probs[m] = std::pow(p[m], alpha) / tot;
+  return KVQ_OK;
+}
+
 double kvq_bits_per_elem(const kvq_params* p, int metadata) {
   if (!p) return -1.0;
   const double n = double(p->n_kv_heads) * p->head_dim;

@@ -41,6 +41,7 @@ _SIGS = {
     "kvq_plan_destroy": (None, [_P]),
     "kvq_plan_tables": (_I32, [_P, ctypes.c_int, _P, _P, _P]),
     "kvq_plan_lambda_grid": (_I32, [_P, _P]),
+    "kvq_model_probs": (_I32, [_I32, _I32, ctypes.c_double, _P]),
     "kvq_bits_per_elem": (ctypes.c_double, [ctypes.POINTER(kvq_params), ctypes.c_int]),
     "kvq_containers_for_budget": (_I32, [ctypes.c_double, _I32, _I32, _I32,
                                          ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
@@ -139,6 +140,13 @@ class Plan:
         _check("kvq_workspace_bytes", lib().kvq_workspace_bytes(
             self.handle, op, n_seqs, seq_len, n_q_heads, ctypes.byref(b)))
         return b.value
+
+
+def kvq_model_probs(levels, n, alpha=1.0):
+    """Model probabilities of the `levels` symbols (list of floats)."""
+    out = (ctypes.c_double * levels)()
+    _check("kvq_model_probs", lib().kvq_model_probs(levels, n, float(alpha), out))
+    return list(out)
 
 
 def kvq_containers_for_budget(bits_per_elem, n_kv_heads, head_dim, mean_window):

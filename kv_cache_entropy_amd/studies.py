@@ -1,0 +1,215 @@
+"""Synthetic rate-distortion and drift studies on the GPU path.
+
+    python -m kv_cache_entropy_amd.studies [--seqs 16] [--tokens 1024] [--json out.json]
+
+Analogues, on seeded synthetic KV, of the measurements of the page
+"D-Quant: Driftable Entropy Coding for KV Cache Quantization":
+  * §3.2 Table 1: NMSE, coding gain (log2 M - H) and normal gap (CE - H) of
+    8-level per-token grids after rotation and key-mean removal;
+  * §3.2 Table 2: NMSE against the alphabet size at fixed K / V containers
+    (2.68 / 1.84 bits per value);
+  * §5.4 Figure 4 (middle, right): error against the storage budget at 8/6
+    levels, and against the K/V split of a fixed 2.26-bit budget;
+  * Appendix C: changed-symbol fractions after drift and the extra rate of the
+    analytic model against the measured symbol distributions.
+Containers are written and read by libkvq (the same kernels the tests check
+bit-exactly against the oracle); torch only measures errors and histograms.
+The inputs are the Llama-shaped GQA workload's distribution (per-channel key
+means, unit-variance values), not captured KV: the numbers characterise the
+coder on near-Gaussian data and are not the page's model-accuracy results.
+"""
+
+import argparse
+import json
+import math
+import sys
+
+import torch
+
+from . import kvq, synth
+
+
+def hadamard(d, device):
+    H = torch.ones(1, 1, dtype=torch.float64)
+    while H.shape[0] < d:
+        H = torch.cat([torch.cat([H, H], 1), torch.cat([H, -H], 1)], 0)
+    return (H / math.sqrt(d)).to(device)
+
+
+class Sample:
+    """Seeded K, V, q of a few sequences, plus exact references."""
+
+    def __init__(self, seqs, tokens, device="cuda"):
+        self.w = synth.WORKLOADS["gqa"]
+        self.seqs = list(range(seqs))
+        self.k, self.v = synth.cache_inputs(self.w, device, self.seqs, (0, tokens))
+        self.q = synth.queries(self.w, device, self.seqs)
+        self.S, self.T = len(self.seqs), tokens
+        w = self.w
+        H = hadamard(w.head_dim, device)
+        rot = lambda x: (x.double().reshape(self.S, self.T, w.n_kv_heads, w.head_dim) @ H).reshape(
+            self.S, self.T, w.n)
+        self.k_rot, self.v_rot = rot(self.k), rot(self.v)
+        self.H = H
+        self.exact = self.attention(self.k.double(), self.v.double())
+
+    def attention(self, K, V):
+        w = self.w
+        G = w.n_q_heads // w.n_kv_heads
+        q = self.q.double().reshape(self.S, w.n_kv_heads, G, w.head_dim)
+        K = K.reshape(self.S, self.T, w.n_kv_heads, w.head_dim).permute(0, 2, 1, 3)
+        V = V.reshape(self.S, self.T, w.n_kv_heads, w.head_dim).permute(0, 2, 1, 3)
+        a = torch.softmax(q @ K.transpose(-1, -2) / math.sqrt(w.head_dim), dim=-1)
+        return (a @ V).reshape(self.S, w.n_q_heads, w.head_dim)
+
+
+def run_config(sm, mk, mv, ck, cv, attention=True):
+    """Encodes the sample with one format; returns errors and symbol statistics."""
+    w = sm.w
+    try:
+        plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4)
+    except kvq.KvqError as e:
+        if e.status == -2:            # KVQ_EINFEASIBLE: the alphabet does not fit
+            return None
+        raise
+    c = kvq.alloc_cache(plan, sm.S, sm.T)
+    stats = torch.zeros(8, dtype=torch.int64, device="cuda")
+    kvq.kvq_encode_streams(plan, sm.k, sm.v, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
+                           c["k_mean_q"], c["k_mean_scale"], stats=stats)
+    out = {"levels": [mk, mv], "containers": [ck, cv], "bits_per_elem": plan.bits_per_elem(True)}
+    st = stats.cpu().tolist()
+    nsym = sm.S * sm.T * w.n
+    out["changed_k"], out["changed_v"] = st[2] / nsym, st[6] / nsym
+    out["fallbacks"] = st[0] + st[1] + st[4] + st[5]
+    mu = (c["k_mean_q"].double() * c["k_mean_scale"].view(torch.float16).double()[..., None])
+    mu_tok = mu.repeat_interleave(128, dim=1)
+    for side, key, so_key, ref in ((0, "k_cont", "k_so", sm.k_rot), (1, "v_cont", "v_so", sm.v_rot)):
+        sym = torch.empty(sm.S, sm.T, w.n, dtype=torch.uint8, device="cuda")
+        kvq.kvq_decode_symbols(plan, side, c[key], sym)
+        so = c[so_key].view(torch.float16).double()
+        rec = so[..., 0:1] * sym.double() + so[..., 1:2]
+        if side == 0:
+            rec = rec + mu_tok
+        name = "k" if side == 0 else "v"
+        out[f"nmse_{name}"] = float(((rec - ref) ** 2).sum() / (ref ** 2).sum())
+        M = mk if side == 0 else mv
+        hist = torch.bincount(sym.flatten().long(), minlength=M).double()
+        ph = hist / hist.sum()
+        model = torch.tensor(kvq.kvq_model_probs(M, w.n, 1.0), dtype=torch.float64, device="cuda")
+        f, _, _ = plan.tables(side)
+        table = torch.tensor(f, dtype=torch.float64, device="cuda") / 256.0
+        nz = ph > 0
+        H = float(-(ph[nz] * torch.log2(ph[nz])).sum())
+        out[f"entropy_{name}"] = H
+        out[f"coding_gain_{name}"] = math.log2(M) - H
+        out[f"model_gap_{name}"] = float(-(ph[nz] * torch.log2(model[nz])).sum()) - H
+        out[f"table_gap_{name}"] = float(-(ph[nz] * torch.log2(table[nz])).sum()) - H
+        out[f"hist_{name}"] = [round(float(x), 5) for x in ph]
+        if side == 0:
+            khat_rot = rec
+        else:
+            vhat_rot = rec
+    if attention and mk <= 9 and mv <= 8:
+        o = torch.empty(sm.S, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+        o32 = torch.empty_like(o, dtype=torch.float32)
+        ws = torch.empty(plan.workspace_bytes(1, sm.S, sm.T, w.n_q_heads), dtype=torch.uint8, device="cuda")
+        kvq.kvq_decode_attention(plan, sm.q, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
+                                 c["k_mean_q"], c["k_mean_scale"], o, ws, out_f32=o32)
+        err = (o32.double() - sm.exact).norm(dim=-1) / sm.exact.norm(dim=-1)
+        out["attn_rel_err"] = float(err.mean())
+        # the same attention from the reconstructed cache in float64 (isolates the
+        # kernel's own arithmetic from the quantisation error)
+        kh = (khat_rot.reshape(sm.S, sm.T, w.n_kv_heads, w.head_dim) @ sm.H).reshape(sm.S, sm.T, w.n)
+        vh = (vhat_rot.reshape(sm.S, sm.T, w.n_kv_heads, w.head_dim) @ sm.H).reshape(sm.S, sm.T, w.n)
+        ref_q = sm.attention(kh, vh)
+        out["attn_kernel_vs_dequant"] = float(((o32.double() - ref_q).norm(dim=-1) / ref_q.norm(dim=-1)).max())
+    torch.cuda.synchronize()
+    return out
+
+
+def fmt(x, spec=".4f"):
+    return "—" if x is None else format(x, spec)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--seqs", type=int, default=16)
+    ap.add_argument("--tokens", type=int, default=1024)
+    ap.add_argument("--json", default=None)
+    args = ap.parse_args(argv)
+    if not torch.cuda.is_available():
+        sys.exit("the studies run the HIP library and need a GPU")
+    sm = Sample(args.seqs, args.tokens)
+    res = {"sample": f"gqa distribution, sequences 0..{args.seqs - 1}, {args.tokens} tokens each"}
+    print(f"# Synthetic studies ({res['sample']})\n")
+
+    # Table 1 analogue: 8 levels, a container large enough that drift never acts
+    t1 = run_config(sm, 8, 8, 400, 400)
+    res["table1"] = t1
+    print("## 8-level grids, no budget pressure (Table 1 analogue)\n")
+    print("| side | NMSE | entropy H (bits) | coding gain log2 M − H | normal gap CE − H | sharpened-table gap |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for s in ("k", "v"):
+        print(f"| {s.upper()} | {t1['nmse_' + s]:.4%} | {t1['entropy_' + s]:.4f} | {t1['coding_gain_' + s]:.4f} | "
+              f"{t1['model_gap_' + s]:.5f} | {t1['table_gap_' + s]:.5f} |")
+
+    # Table 2 analogue: alphabet size at fixed containers
+    print("\n## NMSE against the alphabet at K 331 B (2.68 bits/value) and V 231 B (1.84) (Table 2 analogue)\n")
+    print("| levels | K NMSE | V NMSE |")
+    print("|---:|---:|---:|")
+    res["table2"] = []
+    for M in (2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 14, 16):
+        rk = run_config(sm, M, 2, 331, 231, attention=False)
+        rv = run_config(sm, 2, M, 331, 231, attention=False)
+        nk = rk["nmse_k"] if rk else None
+        nv = rv["nmse_v"] if rv else None
+        res["table2"].append({"levels": M, "nmse_k": nk, "nmse_v": nv})
+        print(f"| {M} | {fmt(nk, '.4%')} | {fmt(nv, '.4%')} |")
+
+    # Figure 4 middle analogue: budget sweep at 8/6 levels
+    print("\n## Storage budget at 8/6 levels (Figure 4 middle analogue)\n")
+    print("| bits/value | C_K/C_V | K NMSE | V NMSE | attention rel. error | K changed | V changed | kernel vs dequant |")
+    print("|---:|---|---:|---:|---:|---:|---:|---:|")
+    res["budget"] = []
+    for b in (1.75, 2.0, 2.26, 2.5, 3.0, 3.5, 4.0):
+        ck, cv = kvq.kvq_containers_for_budget(b, 8, 128, 128)
+        r = run_config(sm, 8, 6, ck, cv)
+        res["budget"].append(dict(budget=b, **(r or {})))
+        if r is None:
+            print(f"| {b} | {ck}/{cv} | — | — | — | — | — | — |")
+            continue
+        print(f"| {r['bits_per_elem']:.3f} | {ck}/{cv} | {r['nmse_k']:.4%} | {r['nmse_v']:.4%} | "
+              f"{r['attn_rel_err']:.4%} | {r['changed_k']:.3%} | {r['changed_v']:.3%} | "
+              f"{r['attn_kernel_vs_dequant']:.1e} |")
+
+    # Figure 4 right analogue: K/V split at 2.26 bits per value
+    print("\n## K/V split of 562 container bytes (2.26 bits/value) (Figure 4 right analogue)\n")
+    print("| C_K/C_V | K NMSE | V NMSE | attention rel. error |")
+    print("|---|---:|---:|---:|")
+    res["split"] = []
+    for ck in (251, 291, 331, 371, 411):
+        cv = 562 - ck
+        r = run_config(sm, 8, 6, ck, cv)
+        res["split"].append(dict(ck=ck, cv=cv, **(r or {})))
+        if r is None:
+            print(f"| {ck}/{cv} | — | — | — |")
+            continue
+        print(f"| {ck}/{cv} | {r['nmse_k']:.4%} | {r['nmse_v']:.4%} | {r['attn_rel_err']:.4%} |")
+
+    # Appendix C analogue: the default format
+    d = next(r for r in res["budget"] if r["budget"] == 2.26)
+    print("\n## Default format 331/231 B, 8/6 levels (Appendix C analogue)\n")
+    print(f"* changed symbols after drift: K {d['changed_k']:.3%}, V {d['changed_v']:.3%}; "
+          f"fallbacks {d['fallbacks']}")
+    print(f"* extra rate of the analytic model over the measured symbol distribution: "
+          f"K {d['model_gap_k']:.4f}, V {d['model_gap_v']:.4f} bits/value; of the sharpened "
+          f"coding table: K {d['table_gap_k']:.4f}, V {d['table_gap_v']:.4f}")
+    print(f"* measured K histogram {d['hist_k']}")
+    print(f"* measured V histogram {d['hist_v']}")
+    if args.json:
+        with open(args.json, "w") as fh:
+            json.dump(res, fh, indent=1)
+
+
+if __name__ == "__main__":
+    main()

@@ -125,3 +125,12 @@ def test_append_and_residual_entry_points_reject_bad_arguments():
     assert attend(100, 0) == -1                       # not a multiple of W
     assert attend(2048, 0) == -1                      # more tokens than the capacity
     assert plan.workspace_bytes(1, 2, 0, 32) > 0      # a tail-only call still needs partials
+
+
+@pytest.mark.parametrize("M,n,alpha", [(8, 1024, 1.0), (6, 1024, 1.4), (8, 128, 1.0), (3, 1024, 2.0)])
+def test_model_probs_match_oracle(M, n, alpha):
+    _lib()
+    got = np.array(kvq.kvq_model_probs(M, n, alpha))
+    p = O.order_stat_probs(M, n)
+    want = O.sharpen(p, alpha) if alpha != 1.0 else p
+    assert np.max(np.abs(got - want)) <= 1e-9
