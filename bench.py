@@ -130,6 +130,16 @@ def main():
     torch.cuda.synchronize()
     encode_ms = e0.elapsed_time(e1) / args.encode_reps
     log(f"[bench] encode {encode_ms:.1f} ms for {S * T} token-layers")
+    # the fixed-width comparator of the same cache (page Appendix B: same
+    # preprocessing, nearest rounding at 6/3 levels, power-of-two widths)
+    fw_cmp = None
+    if w.n % 1024 == 0 and w.dtype == "bf16":
+        fk, fv = kvq.kvq_fixed_width_container_bytes(6, n), kvq.kvq_fixed_width_container_bytes(3, n)
+        plan_fw = kvq.Plan(w.n_kv_heads, d, 6, 3, fk, fv, 128, 1.4)
+        cache_fw = kvq.alloc_cache(plan_fw, S, T, dev)
+        kvq.kvq_encode_fixed_width(plan_fw, k, v, cache_fw["k_cont"], cache_fw["v_cont"], cache_fw["k_so"],
+                                   cache_fw["v_so"], cache_fw["k_mean_q"], cache_fw["k_mean_scale"])
+        torch.cuda.synchronize()
     # samples for the CPU baseline, copied before the inputs are freed
     base_seqs = [0, S - 1] if S > 1 else [0]
     base_tokens = min(T, 512)
@@ -220,6 +230,41 @@ def main():
         log(f"[bench] streaming: prefix {n_pre} + bf16 tail {r_len}: {ex_ms:.3f} ms/step; "
             f"append of one {W}-token window per sequence {app_ms:.3f} ms")
 
+    if w.n % 1024 == 0 and w.dtype == "bf16":
+        ws_fw = torch.empty(plan_fw.workspace_bytes(1, S, T, Hq), dtype=torch.uint8, device=dev)
+
+        def step_fw():
+            kvq.kvq_decode_attention_fixed_width(plan_fw, q, cache_fw["k_cont"], cache_fw["v_cont"],
+                                                 cache_fw["k_so"], cache_fw["v_so"], cache_fw["k_mean_q"],
+                                                 cache_fw["k_mean_scale"], out, ws_fw)
+
+        for _ in range(args.warmup):
+            step_fw()
+        torch.cuda.synchronize()
+        kvq.kvq_timing_collect()
+        kvq.kvq_timing_enable(True)
+        t0.record()
+        for _ in range(args.steps):
+            step_fw()
+        t1.record()
+        torch.cuda.synchronize()
+        kvq.kvq_timing_enable(False)
+        fw_ms = t0.elapsed_time(t1) / args.steps
+        fkms, fkl = kvq.kvq_timing_collect()
+        fw_kernel_ms = fkms / max(1, fkl)
+        fw_kernel_bytes = S * T * (fk + fv + 8)
+        charged = (n * (math.log2(6) + math.log2(3)) / 8 + 8 + (n + 2) / 128) * 8 / (2 * n)
+        fw_cmp = {"levels": [6, 3], "containers": [fk, fv],
+                  "bits_per_elem_stored": round(plan_fw.bits_per_elem(True), 4),
+                  "bits_per_elem_charged_ideal": round(charged, 4),
+                  "step_ms": round(fw_ms, 4), "kernel_ms": round(fw_kernel_ms, 4),
+                  "kernel_gb_per_s": round(fw_kernel_bytes / (fw_kernel_ms * 1e-3) / 1e9, 2),
+                  "kernel_frac_of_hbm_peak": round(fw_kernel_bytes / (fw_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "token_layers_per_s": round(S * T / (fw_ms * 1e-3), 1)}
+        log(f"[bench] fixed-width 6/3 comparator: step {fw_ms:.3f} ms, kernel {fw_kernel_ms:.3f} ms "
+            f"({fw_cmp['kernel_gb_per_s']:.1f} GB/s of {fk + fv} B containers)")
+        del cache_fw
+
     # ---- CPU baseline: the oracle's read side on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
@@ -270,6 +315,7 @@ def main():
                         "symbols_per_side": S * T * n},
         "rotated_copies": copies,
         "streaming": streaming,
+        "comparator_fixed_width": fw_cmp,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

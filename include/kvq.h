@@ -195,6 +195,42 @@ kvq_status kvq_decode_attention_ex(const kvq_plan* plan, const void* q, int32_t 
                                    void* workspace, size_t workspace_bytes,
                                    void* hip_stream);
 
+/* Fixed-width comparator ([D-Quant] Appendix B: same preprocessing, symbols
+ * by nearest-level rounding instead of drift, no entropy coding).  Each symbol
+ * takes b bits, b the smallest of 1, 2, 4, 8 with 2^b >= levels (the page
+ * charges the ideal log2 M bits; no fixed width can hold every symbol in
+ * that), so a stream is n b / 8 bytes: symbol i = 4c + r sits in byte r of
+ * little-endian dword c / (8/b), bits b (c mod 8/b) .. + b.
+ * kvq_fixed_width_container_bytes gives n b / 8 (KVQ_EINVAL unless n b is a
+ * multiple of 32). */
+kvq_status kvq_fixed_width_container_bytes(int32_t levels, int32_t n, int32_t* bytes);
+
+/* Encodes like kvq_encode_streams (same tensors and layout) in the
+ * fixed-width format; the plan's container sizes must equal the fixed-width
+ * sizes of its alphabets (KVQ_EINVAL otherwise), e.g. 6/3 levels -> 512/256
+ * bytes for n = 1024.  KVQ_EUNSUPPORTED unless n >= 1024 and (n/64) b is a
+ * multiple of 32.  The plan's rANS tables are not used. */
+kvq_status kvq_encode_fixed_width(const kvq_plan* plan, const void* k, const void* v,
+                                  kvq_dtype in_dtype, int64_t n_seqs, int64_t seq_len,
+                                  uint8_t* k_cont, uint8_t* v_cont,
+                                  uint16_t* k_so, uint16_t* v_so,
+                                  int8_t* k_mean_q, uint16_t* k_mean_scale,
+                                  void* hip_stream);
+
+/* Fused decode attention over fixed-width containers: arguments, workspace
+ * and output as kvq_decode_attention.  KVQ_EUNSUPPORTED unless d = 128, Hkv
+ * and Hq / Hkv are in {1, 2, 4, 8}, both alphabets have at most 8 levels,
+ * (b_K, b_V) is (4, 2), (4, 4), (2, 2) or (2, 1), W >= 64 and seq_len is a
+ * multiple of 64. */
+kvq_status kvq_decode_attention_fixed_width(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                                            const uint8_t* k_cont, const uint8_t* v_cont,
+                                            const uint16_t* k_so, const uint16_t* v_so,
+                                            const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                                            int64_t n_seqs, int64_t seq_len, float softmax_scale,
+                                            void* out, float* out_f32,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* hip_stream);
+
 /* Decodes containers back to symbol indices (Appendix A, Algorithm 2); a
  * verification helper.  side 0 = K table, 1 = V table.
  *   cont      [n_streams, C] bytes;  symbols out [n_streams, n] uint8

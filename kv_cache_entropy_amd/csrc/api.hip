@@ -80,6 +80,14 @@ kvq::EncTabs enc_tabs(const kvq_plan* plan, int side) {
   return e;
 }
 
+// Bits per symbol of the fixed-width comparator: the smallest of 1, 2, 4, 8
+// that holds `levels` symbols (0 if none does).
+int fw_bits(int levels) {
+  for (int b = 1; b <= 8; b <<= 1)
+    if ((1 << b) >= levels) return b;
+  return 0;
+}
+
 // Streams per encode workgroup: the largest of 32/16/8/4 that divides the
 // tokens per sequence (a workgroup's streams then lie in one sequence) and
 // keeps the symbol and container staging under 56 KiB.
@@ -165,7 +173,8 @@ namespace {
 kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_dtype in_dtype,
                        int64_t n_seqs, int64_t n_tokens, int64_t capacity, int64_t t_off,
                        uint8_t* k_cont, uint8_t* v_cont, uint16_t* k_so, uint16_t* v_so,
-                       int8_t* k_mean_q, uint16_t* k_mean_scale, uint64_t* stats, void* hip_stream) {
+                       int8_t* k_mean_q, uint16_t* k_mean_scale, uint64_t* stats, void* hip_stream,
+                       bool fixed_width = false) {
   if (!plan || !k || !v || !k_cont || !v_cont || !k_so || !v_so || !k_mean_q || !k_mean_scale)
     return KVQ_EINVAL;
   if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return KVQ_EINVAL;
@@ -179,6 +188,16 @@ kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_d
   if (n_seqs < 1 || n_tokens < W || n_tokens % W) return KVQ_EINVAL;
   if (t_off < 0 || t_off % W || capacity % W || t_off + n_tokens > capacity) return KVQ_EINVAL;
   if (n % 64 || n > 4096 || W < 4) return KVQ_EUNSUPPORTED;
+  int fwb[2] = {0, 0};
+  if (fixed_width) {
+    fwb[0] = fw_bits(P.levels_k);
+    fwb[1] = fw_bits(P.levels_v);
+    for (int side = 0; side < 2; ++side) {
+      const int C = side == 0 ? P.container_bytes_k : P.container_bytes_v;
+      if (C != n * fwb[side] / 8) return KVQ_EINVAL;            // not the fixed-width size
+      if (((n / 64) * fwb[side]) % 32 || n / 64 < 16) return KVQ_EUNSUPPORTED;
+    }
+  }
   const int64_t n_streams = n_seqs * n_tokens;
   const int spw_k = pick_spw(n_tokens, n, P.container_bytes_k);
   const int spw_v = pick_spw(n_tokens, n, P.container_bytes_v);
@@ -219,6 +238,7 @@ kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_d
     ea.d = P.head_dim;
     ea.hscale = plan->hadamard_scale;
     ea.spw = side == 0 ? spw_k : spw_v;
+    ea.fw_bits = fwb[side];
     ea.tabs = enc_tabs(plan, side);
     if (kvq::launch_encode(ea, n_streams, stream) != hipSuccess) return KVQ_EDEVICE;
   }
@@ -235,7 +255,7 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
                           int64_t n_seqs, int64_t capacity, int64_t n_tokens, const void* res_k,
                           const void* res_v, int64_t res_cap, int64_t res_len, float softmax_scale,
                           void* out, float* out_f32, void* workspace, size_t workspace_bytes,
-                          void* hip_stream) {
+                          void* hip_stream, bool fixed_width = false) {
   if (!plan || !q || !out || !workspace) return KVQ_EINVAL;
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EINVAL;
   if (out_f32 && !aligned16(out_f32)) return KVQ_EINVAL;
@@ -255,8 +275,14 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
     if (!res_k || !res_v || !aligned16(res_k) || !aligned16(res_v) || res_cap < res_len) return KVQ_EINVAL;
   }
   const int G = n_q_heads / Hkv;
-  if (n_tokens % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W))
+  const int bk = fw_bits(P.levels_k), bv = fw_bits(P.levels_v);
+  if (fixed_width) {
+    if (P.container_bytes_k != plan->n * bk / 8 || P.container_bytes_v != plan->n * bv / 8) return KVQ_EINVAL;
+    if (n_tokens % 64 || W < 64 || !kvq::attention_fw_supported(n_q_heads, G, d, bk, bv, P.levels_k, P.levels_v))
+      return KVQ_EUNSUPPORTED;
+  } else if (n_tokens % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W)) {
     return KVQ_EUNSUPPORTED;
+  }
   if (n_seqs > 65535) return KVQ_EUNSUPPORTED;
   // the attention kernel addresses one sequence's containers with 32-bit offsets
   if (int64_t(n_tokens) * std::max(P.container_bytes_k, P.container_bytes_v) + 16 > INT32_MAX)
@@ -326,7 +352,9 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
     }
     size_t slot = 0;
     const bool timed = timer_begin(stream, &slot);
-    if (kvq::launch_attention2(aa, n_seqs, n_q_heads, G, stream) != hipSuccess) return KVQ_EDEVICE;
+    const hipError_t e = fixed_width ? kvq::launch_attention_fw(aa, n_seqs, n_q_heads, G, bk, bv, stream)
+                                     : kvq::launch_attention2(aa, n_seqs, n_q_heads, G, stream);
+    if (e != hipSuccess) return KVQ_EDEVICE;
     if (timed) timer_end(stream, slot);
   }
   if (res_len > 0) {
@@ -406,6 +434,35 @@ kvq_status kvq_decode_attention_ex(const kvq_plan* plan, const void* q, int32_t 
   return attention_impl(plan, q, n_q_heads, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, n_seqs,
                         cache_capacity, n_tokens, res_k, res_v, res_capacity, res_len, softmax_scale, out,
                         out_f32, workspace, workspace_bytes, hip_stream);
+}
+
+kvq_status kvq_fixed_width_container_bytes(int32_t levels, int32_t n, int32_t* bytes) {
+  if (!bytes || levels < 2 || levels > 256 || n < 1) return KVQ_EINVAL;
+  const int b = fw_bits(levels);
+  if ((int64_t(n) * b) % 32) return KVQ_EINVAL;
+  *bytes = n * b / 8;
+  return KVQ_OK;
+}
+
+kvq_status kvq_encode_fixed_width(const kvq_plan* plan, const void* k, const void* v,
+                                  kvq_dtype in_dtype, int64_t n_seqs, int64_t seq_len,
+                                  uint8_t* k_cont, uint8_t* v_cont, uint16_t* k_so, uint16_t* v_so,
+                                  int8_t* k_mean_q, uint16_t* k_mean_scale, void* hip_stream) {
+  return encode_impl(plan, k, v, in_dtype, n_seqs, seq_len, seq_len, 0, k_cont, v_cont, k_so, v_so,
+                     k_mean_q, k_mean_scale, nullptr, hip_stream, true);
+}
+
+kvq_status kvq_decode_attention_fixed_width(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                                            const uint8_t* k_cont, const uint8_t* v_cont,
+                                            const uint16_t* k_so, const uint16_t* v_so,
+                                            const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                                            int64_t n_seqs, int64_t seq_len, float softmax_scale,
+                                            void* out, float* out_f32, void* workspace,
+                                            size_t workspace_bytes, void* hip_stream) {
+  if (seq_len < 1) return KVQ_EINVAL;
+  return attention_impl(plan, q, n_q_heads, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, n_seqs,
+                        seq_len, seq_len, nullptr, nullptr, 0, 0, softmax_scale, out, out_f32, workspace,
+                        workspace_bytes, hip_stream, true);
 }
 
 kvq_status kvq_decode_symbols(const kvq_plan* plan, int side, const uint8_t* cont,

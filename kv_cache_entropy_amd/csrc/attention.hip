@@ -839,6 +839,208 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
       }
 }
 
+// ------------------------------------------------ fixed-width comparator
+// [D-Quant] Appendix B compares the entropy-coded container with fixed-width
+// symbols at the same preprocessing.  Symbol i = 4c + r of a stream sits in
+// byte r of dword c / (8/B), bits B (c mod 8/B) .. + B, so the 4 symbols of
+// channel quad c are (dword >> shift) & mask with one symbol per byte, and a
+// KV head's 128 symbols are 4 B contiguous dwords at a fixed offset.  Same
+// contractions and softmax as the entropy-coded kernels (one wave per split,
+// K head g then V head g); the decoder is a shift and a mask per 4 symbols.
+template <int N>
+__device__ inline uint32_t dword_of(const uint4 (&v)[N], int i) {
+  const uint4 q = v[i / 4];
+  return (i % 4 == 0) ? q.x : (i % 4 == 1) ? q.y : (i % 4 == 2) ? q.z : q.w;
+}
+
+template <int G, int HKV, int BK, int BV>
+__global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
+  constexpr int HQ = G * HKV;
+  constexpr int NGM = (G + 3) / 4;
+  constexpr int NW = NGM * 4;
+  constexpr int KW = 128 * BK / 32, VW = 128 * BV / 32;    // dwords per head
+  constexpr int KPER = 8 / BK, VPER = 8 / BV;              // channel quads per dword
+  constexpr uint32_t KMASK = ((1u << BK) - 1u) * 0x01010101u;
+  constexpr uint32_t VMASK = ((1u << BV) - 1u) * 0x01010101u;
+  __shared__ __align__(16) uint8_t vch[64 * kChunk8Stride];
+  __shared__ __align__(16) uint16_t wts[2][NW][64];       // [hi/lo][slot][token]
+  __shared__ float runM[HQ], runL[HQ], runZ[HQ];
+  __shared__ float affS[HQ], affQ[HQ], affM[HQ];
+
+  const int lane = threadIdx.x;
+  const int64_t s = blockIdx.y;
+  const int split = blockIdx.x;
+  for (int h = lane; h < HQ; h += 64) {
+    runM[h] = -__builtin_inff();
+    runL[h] = 0.f;
+    runZ[h] = 0.f;
+  }
+  for (int i = lane; i < 2 * NW * 64; i += 64) (&wts[0][0][0])[i] = 0;
+  const uint32_t lutLoK = a.hbk[0] | (a.hbk[1] << 8) | (a.hbk[2] << 16) | (a.hbk[3] << 24);
+  const uint32_t lutHiK = a.hbk[4] | (a.hbk[5] << 8) | (a.hbk[6] << 16) | (a.hbk[7] << 24);
+  const uint32_t lutLoV = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
+  const uint32_t lutHiV = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
+  wave_lds_fence();
+
+  float4_t O[HKV][2][NGM];
+#pragma unroll
+  for (int g = 0; g < HKV; ++g)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) O[g][c][m] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t tb = int64_t(split) * a.tokens_per_split;
+  const int64_t te = tb + a.tokens_per_split < a.T ? tb + a.tokens_per_split : a.T;
+  const uint4* qop = a.qop + s * (HKV * NGM * 32 * 4);
+  const float* qscale = a.qscale + s * HQ;
+  const float* qsum = a.qsum + s * HQ;
+  const float* qmu = a.qmu + s * HQ * a.nW;
+  const int qn = lane & 3;
+
+  for (int64_t t0 = tb; t0 < te; t0 += 64) {
+    const int64_t row = s * a.T_cap + t0 + lane;
+    const float sk = h2f(a.k_so[2 * row]), ok = h2f(a.k_so[2 * row + 1]);
+    const float sv = h2f(a.v_so[2 * row]), ov = h2f(a.v_so[2 * row + 1]);
+    const int64_t wdx = t0 >> a.log2W;
+    for (int h = lane; h < HQ; h += 64) {
+      affS[h] = qscale[h];
+      affQ[h] = qsum[h];
+      affM[h] = qmu[h * a.nW + wdx];
+    }
+    wave_lds_fence();
+    const uint32_t* kr = reinterpret_cast<const uint32_t*>(a.k_cont + row * a.CK);
+    const uint4* vr = reinterpret_cast<const uint4*>(a.v_cont + row * a.CV);
+#pragma unroll
+    for (int g = 0; g < HKV; ++g) {
+      // this head's V bits arrive while its K levels are contracted
+      uint4 vc[VW / 4];
+#pragma unroll
+      for (int j = 0; j < VW / 4; ++j) vc[j] = vr[g * (VW / 4) + j];
+      // ---- QK^T on the K levels of head g: 8 blocks of 4 channel quads, the
+      // K bits of a block (BK / 2 dwords) loaded one block ahead
+      float4_t D[NGM];
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) D[m] = float4_t{0.f, 0.f, 0.f, 0.f};
+      const uint4* qg = qop + g * (NGM * 32 * 4) + qn;
+      const uint32_t* kh = kr + g * KW;
+      constexpr int KB = BK / 2;                               // dwords per block
+      uint32_t kb[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) kb[j] = kh[j];
+      uint4 qa[NGM];
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) qa[m] = qg[(m * 32) * 4];
+#pragma unroll 1
+      for (int blk = 0; blk < 8; ++blk) {
+        const int bn = blk + 1 < 8 ? blk + 1 : 7;
+        uint32_t kbn[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) kbn[j] = kh[bn * KB + j];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int c = blk * 4 + cc;
+          const int cn = c + 1 < 32 ? c + 1 : 31;
+          uint4 qb[NGM];
+#pragma unroll
+          for (int m = 0; m < NGM; ++m) qb[m] = qg[(m * 32 + cn) * 4];
+          const uint32_t sym = (kb[cc / KPER] >> (BK * (cc % KPER))) & KMASK;
+          const uint32_t hb = __builtin_amdgcn_perm(lutHiK, lutLoK, sym);
+          const half4_t B = as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu),
+                                     __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
+#pragma unroll
+          for (int m = 0; m < NGM; ++m) {
+            D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(qa[m].x, qa[m].y), B, D[m], 0, 0, 0);
+            D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(qa[m].z, qa[m].w), B, D[m], 0, 0, 0);
+            qa[m] = qb[m];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) kb[j] = kbn[j];
+      }
+      // ---- online softmax of this KV head's query heads over the tile
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const int m = v / 4, ii = v % 4;
+        float whi = 0.f, wlo = 0.f;
+        if (v < G) {
+          const int h = g * G + v;
+          const float lg = a.tau * (sk * (D[m][ii] * affS[h]) + ok * affQ[h] + affM[h]);
+          const float tmax = wave_max_dpp(lg);
+          const float Mo = runM[h], Lo = runL[h], Zo = runZ[h];
+          const float Mn = fmaxf(Mo, tmax);
+          const float al = __expf(Mo - Mn);
+          const float p = __expf(lg - Mn);
+          const float ls = wave_sum_dpp(p);
+          const float zs = wave_sum_dpp(p * ov);
+          runM[h] = Mn;
+          runL[h] = Lo * al + ls;
+          runZ[h] = Zo * al + zs;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) O[g][c][m][ii] *= al;
+          const float wt = p * sv;
+          const __half hh = __float2half_rn(wt);
+          whi = wt;
+          wlo = wt - __half2float(hh);
+        }
+        wts[0][v][lane] = __half_as_ushort(__float2half_rn(whi));
+        wts[1][v][lane] = __half_as_ushort(__float2half_rn(wlo));
+      }
+      // ---- V levels of head g, 64 channels at a time, then PV
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        wave_lds_fence();
+#pragma unroll
+        for (int cq = 0; cq < 16; ++cq) {
+          const int c = ch * 16 + cq;
+          const uint32_t sym = (dword_of(vc, c / VPER) >> (BV * (c % VPER))) & VMASK;
+          uint8_t* col = vch + (4 * cq) * kChunk8Stride + lane;
+          col[0] = uint8_t(sym);
+          col[kChunk8Stride] = uint8_t(sym >> 8);
+          col[2 * kChunk8Stride] = uint8_t(sym >> 16);
+          col[3 * kChunk8Stride] = uint8_t(sym >> 24);
+        }
+        wave_lds_fence();
+#pragma unroll 2
+        for (int tq = 0; tq < 16; ++tq) {
+          const uint32_t idx = *reinterpret_cast<const uint32_t*>(vch + lane * kChunk8Stride + 4 * tq);
+          const uint32_t hb = __builtin_amdgcn_perm(lutHiV, lutLoV, idx);
+          const half4_t B = as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu),
+                                     __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
+#pragma unroll
+          for (int m = 0; m < NGM; ++m) {
+            const uint2 ah = *reinterpret_cast<const uint2*>(&wts[0][m * 4 + qn][4 * tq]);
+            const uint2 al = *reinterpret_cast<const uint2*>(&wts[1][m * 4 + qn][4 * tq]);
+            O[g][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah.x, ah.y), B, O[g][ch][m], 0, 0, 0);
+            O[g][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[g][ch][m], 0, 0, 0);
+          }
+        }
+      }
+      wave_lds_fence();
+    }
+  }
+
+  float* P = a.part + (s * a.part_splits + split) * int64_t(HQ) * (kD + 4);
+#pragma unroll
+  for (int g = 0; g < HKV; ++g)
+#pragma unroll
+    for (int m = 0; m < NGM; ++m)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int v = m * 4 + ii;
+        if (v < G) {
+          const int h = g * G + v;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) P[h * (kD + 4) + c * 64 + lane] = O[g][c][m][ii];
+          if (lane == 0) {
+            P[h * (kD + 4) + kD] = runM[h];
+            P[h * (kD + 4) + kD + 1] = runL[h];
+            P[h * (kD + 4) + kD + 2] = runZ[h];
+          }
+        }
+      }
+}
+
 }  // namespace
 
 hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t stream) {
@@ -886,6 +1088,52 @@ hipError_t launch_attention2(const Attn2Args& a, int64_t S, int Hq, int G, hipSt
     case 2: return launch_attn2_g<2>(a, S, hkv, stream);
     case 4: return launch_attn2_g<4>(a, S, hkv, stream);
     case 8: return launch_attn2_g<8>(a, S, hkv, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int G, int HKV>
+static hipError_t launch_fw_t(const Attn2Args& a, int64_t S, int bk, int bv, hipStream_t stream) {
+  const dim3 grid(a.nsplit, unsigned(S));
+  if (bk == 4 && bv == 2)
+    hipLaunchKernelGGL((attention_fw_kernel<G, HKV, 4, 2>), grid, dim3(64), 0, stream, a);
+  else if (bk == 4 && bv == 4)
+    hipLaunchKernelGGL((attention_fw_kernel<G, HKV, 4, 4>), grid, dim3(64), 0, stream, a);
+  else if (bk == 2 && bv == 2)
+    hipLaunchKernelGGL((attention_fw_kernel<G, HKV, 2, 2>), grid, dim3(64), 0, stream, a);
+  else if (bk == 2 && bv == 1)
+    hipLaunchKernelGGL((attention_fw_kernel<G, HKV, 2, 1>), grid, dim3(64), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_fw_g(const Attn2Args& a, int64_t S, int hkv, int bk, int bv, hipStream_t stream) {
+  switch (hkv) {
+    case 1: return launch_fw_t<G, 1>(a, S, bk, bv, stream);
+    case 2: return launch_fw_t<G, 2>(a, S, bk, bv, stream);
+    case 4: return launch_fw_t<G, 4>(a, S, bk, bv, stream);
+    case 8: return launch_fw_t<G, 8>(a, S, bk, bv, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool attention_fw_supported(int Hq, int G, int d, int bk, int bv, int levels_k, int levels_v) {
+  const int hkv = Hq / G;
+  const bool widths = (bk == 4 && (bv == 2 || bv == 4)) || (bk == 2 && (bv == 2 || bv == 1));
+  return d == kD && (G == 1 || G == 2 || G == 4 || G == 8) && (hkv == 1 || hkv == 2 || hkv == 4 || hkv == 8) &&
+         widths && levels_k <= 8 && levels_v <= 8;
+}
+
+hipError_t launch_attention_fw(const Attn2Args& a, int64_t S, int Hq, int G, int bk, int bv,
+                               hipStream_t stream) {
+  const int hkv = Hq / G;
+  switch (G) {
+    case 1: return launch_fw_g<1>(a, S, hkv, bk, bv, stream);
+    case 2: return launch_fw_g<2>(a, S, hkv, bk, bv, stream);
+    case 4: return launch_fw_g<4>(a, S, hkv, bk, bv, stream);
+    case 8: return launch_fw_g<8>(a, S, hkv, bk, bv, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -50,6 +50,7 @@ struct EncodeArgs {
   int W, n, d;
   float hscale;
   int spw;                     // streams per workgroup (multiple of 4)
+  int fw_bits;                 // 0: rANS + drift; 1/2/4/8: fixed-width comparator
   EncTabs tabs;
 };
 
@@ -239,6 +240,9 @@ hipError_t launch_attention2(const Attn2Args& a, int64_t S, int Hq, int G, hipSt
 bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int window);
 hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream);
 hipError_t launch_residual(const ResidualArgs& a, int64_t S, hipStream_t stream);
+bool attention_fw_supported(int Hq, int G, int d, int bk, int bv, int levels_k, int levels_v);
+hipError_t launch_attention_fw(const Attn2Args& a, int64_t S, int Hq, int G, int bk, int bv,
+                               hipStream_t stream);
 
 }  // namespace kvq
 

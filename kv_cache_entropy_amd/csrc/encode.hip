@@ -169,6 +169,47 @@ __device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& 
   return false;
 }
 
+// Nearest level of every value (lowest index on ties): the lambda -> 0
+// assignment, used alone by the fixed-width comparator.
+template <int NPL>
+__device__ void nearest(const float (&x)[NPL], float s, float o, int levels, uint8_t (&m)[NPL]) {
+  float bestD[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) { bestD[i] = __builtin_inff(); m[i] = 0; }
+  for (int l = 0; l < levels; ++l) {
+    const float rec = __fadd_rn(o, __fmul_rn(s, float(l)));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const float dl = __fsub_rn(x[i], rec);
+      const float D = __fmul_rn(dl, dl);
+      if (D < bestD[i]) { bestD[i] = D; m[i] = uint8_t(l); }
+    }
+  }
+}
+
+// Fixed-width container layout ([D-Quant] Appendix B comparator): symbol
+// i = 4c + r in byte r of dword c / (8/b), bits b (c mod 8/b) .. + b.  A lane's
+// NPL consecutive symbols fill NPL b / 32 whole dwords when NPL is a multiple
+// of 32 / b, which the host checks.
+template <int NPL, int B>
+__device__ void fw_pack_lane(const uint8_t (&m)[NPL], uint32_t* img_words, int lane) {
+  constexpr int per = 8 / B;                   // groups of 4 per dword
+  constexpr int words = NPL * B / 32;
+  static_assert(NPL * B % 32 == 0, "a lane must fill whole dwords");
+#pragma unroll
+  for (int q = 0; q < words; ++q) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < per; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int li = (q * per + k) * 4 + r;    // lane-local symbol index
+        w |= uint32_t(m[li]) << (8 * r + B * k);
+      }
+    img_words[lane * words + q] = w;
+  }
+}
+
 // Least-squares refit in float64 with the fixed summation order (chunk per
 // lane in increasing index from +0, then xor-butterfly 32..1), the guard, and
 // rounding to fp16 through fp32.
@@ -246,8 +287,9 @@ __device__ bool rans_encode_lane(const uint8_t* sym, int n, uint8_t* img, int C,
 // Algorithm 1 on SPW/4 streams in turn (values stay in registers); then SPW
 // lanes rANS-code the streams from LDS and the workgroup copies the SPW
 // contiguous containers out with dword stores.
-template <int NPL>
+template <int NPL, int FWB>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+  constexpr bool FW = FWB != 0;
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ EncShared sh;
   __shared__ uint32_t so_sh[64];
@@ -295,18 +337,25 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const float s = __fdiv_rn(__fsub_rn(mx, mn), float(M - 1));
     const float o = mn;
     uint8_t m[NPL];
-    fb1 += drift<NPL>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
     __half s16, o16;
-    refit<NPL>(x, m, s, o, n, s16, o16);
-    uint8_t nearest[NPL];
-    fb2 += drift<NPL>(x, __half2float(s16), __half2float(o16), sh, M, m, &nearest) ? 1u : 0u;
-    uint32_t ch = 0;
+    if constexpr (FW) {
+      nearest<NPL>(x, s, o, M, m);
+      refit<NPL>(x, m, s, o, n, s16, o16);
+      nearest<NPL>(x, __half2float(s16), __half2float(o16), M, m);
+      if constexpr (FW) fw_pack_lane<NPL, FWB>(m, reinterpret_cast<uint32_t*>(img + size_t(sl) * C), lane);
+    } else {
+      fb1 += drift<NPL>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
+      refit<NPL>(x, m, s, o, n, s16, o16);
+      uint8_t near[NPL];
+      fb2 += drift<NPL>(x, __half2float(s16), __half2float(o16), sh, M, m, &near) ? 1u : 0u;
+      uint32_t ch = 0;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) ch += (m[i] != nearest[i]) ? 1u : 0u;
-    changed += wave_sum_u32(ch);
-    uint8_t* dst = sym + size_t(sl) * n + size_t(lane) * NPL;
+      for (int i = 0; i < NPL; ++i) ch += (m[i] != near[i]) ? 1u : 0u;
+      changed += wave_sum_u32(ch);
+      uint8_t* dst = sym + size_t(sl) * n + size_t(lane) * NPL;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) dst[i] = m[i];
+      for (int i = 0; i < NPL; ++i) dst[i] = m[i];
+    }
     if (lane == 0) so_sh[sl] = uint32_t(__half_as_ushort(s16)) | (uint32_t(__half_as_ushort(o16)) << 16);
   }
   __syncthreads();
@@ -316,7 +365,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   const int64_t ost0 = seq0 * a.T_cap + a.t_off + (stream0 - seq0 * a.T);
   uint32_t overrun = 0;
   if (tid < SPW) {
-    overrun = rans_encode_lane(sym + size_t(tid) * n, n, img + size_t(tid) * C, C, sh) ? 0u : 1u;
+    if constexpr (!FW)
+      overrun = rans_encode_lane(sym + size_t(tid) * n, n, img + size_t(tid) * C, C, sh) ? 0u : 1u;
     reinterpret_cast<uint32_t*>(a.so)[ost0 + tid] = so_sh[tid];
   }
   __syncthreads();
@@ -347,14 +397,32 @@ hipError_t launch_key_mean(const KeyMeanArgs& a, int64_t n_windows, hipStream_t 
 hipError_t launch_encode(const EncodeArgs& a, int64_t n_streams, hipStream_t stream) {
   const size_t lds = size_t(a.spw) * (size_t(a.n) + size_t(a.tabs.container_bytes));
   const dim3 grid(unsigned(n_streams / a.spw)), block(256);
+  if (a.fw_bits) {
+    const int key = (a.n / 64) * 16 + a.fw_bits;
+    switch (key) {
+      case 16 * 16 + 2: hipLaunchKernelGGL((encode_kernel<16, 2>), grid, block, lds, stream, a); break;
+      case 16 * 16 + 4: hipLaunchKernelGGL((encode_kernel<16, 4>), grid, block, lds, stream, a); break;
+      case 16 * 16 + 8: hipLaunchKernelGGL((encode_kernel<16, 8>), grid, block, lds, stream, a); break;
+      case 32 * 16 + 1: hipLaunchKernelGGL((encode_kernel<32, 1>), grid, block, lds, stream, a); break;
+      case 32 * 16 + 2: hipLaunchKernelGGL((encode_kernel<32, 2>), grid, block, lds, stream, a); break;
+      case 32 * 16 + 4: hipLaunchKernelGGL((encode_kernel<32, 4>), grid, block, lds, stream, a); break;
+      case 32 * 16 + 8: hipLaunchKernelGGL((encode_kernel<32, 8>), grid, block, lds, stream, a); break;
+      case 64 * 16 + 1: hipLaunchKernelGGL((encode_kernel<64, 1>), grid, block, lds, stream, a); break;
+      case 64 * 16 + 2: hipLaunchKernelGGL((encode_kernel<64, 2>), grid, block, lds, stream, a); break;
+      case 64 * 16 + 4: hipLaunchKernelGGL((encode_kernel<64, 4>), grid, block, lds, stream, a); break;
+      case 64 * 16 + 8: hipLaunchKernelGGL((encode_kernel<64, 8>), grid, block, lds, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.n / 64) {
-    case 1: hipLaunchKernelGGL(encode_kernel<1>, grid, block, lds, stream, a); break;
-    case 2: hipLaunchKernelGGL(encode_kernel<2>, grid, block, lds, stream, a); break;
-    case 4: hipLaunchKernelGGL(encode_kernel<4>, grid, block, lds, stream, a); break;
-    case 8: hipLaunchKernelGGL(encode_kernel<8>, grid, block, lds, stream, a); break;
-    case 16: hipLaunchKernelGGL(encode_kernel<16>, grid, block, lds, stream, a); break;
-    case 32: hipLaunchKernelGGL(encode_kernel<32>, grid, block, lds, stream, a); break;
-    case 64: hipLaunchKernelGGL(encode_kernel<64>, grid, block, lds, stream, a); break;
+    case 1: hipLaunchKernelGGL((encode_kernel<1, 0>), grid, block, lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((encode_kernel<2, 0>), grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((encode_kernel<4, 0>), grid, block, lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((encode_kernel<8, 0>), grid, block, lds, stream, a); break;
+    case 16: hipLaunchKernelGGL((encode_kernel<16, 0>), grid, block, lds, stream, a); break;
+    case 32: hipLaunchKernelGGL((encode_kernel<32, 0>), grid, block, lds, stream, a); break;
+    case 64: hipLaunchKernelGGL((encode_kernel<64, 0>), grid, block, lds, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -53,6 +53,10 @@ _SIGS = {
                                  _P, _P, _P]),
     "kvq_decode_attention_ex": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P,
                                        _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "kvq_fixed_width_container_bytes": (_I32, [_I32, _I32, ctypes.POINTER(_I32)]),
+    "kvq_encode_fixed_width": (_I32, [_P, _P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "kvq_decode_attention_fixed_width": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64,
+                                                ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "kvq_decode_symbols": (_I32, [_P, ctypes.c_int, _P, _I64, _P, _P, _P]),
     "kvq_status_str": (ctypes.c_char_p, [_I32]),
     "kvq_timing_enable": (_I32, [ctypes.c_int]),
@@ -217,6 +221,38 @@ def kvq_decode_attention_ex(plan, q, cache, n_tokens, res_k, res_v, res_len, out
         _ptr(c.get("v_so")), _ptr(c.get("k_mean_q")), _ptr(c.get("k_mean_scale")), S, cap,
         int(n_tokens), _ptr(res_k), _ptr(res_v), rcap, int(res_len), float(softmax_scale), _ptr(out),
         _ptr(out_f32), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def kvq_fixed_width_container_bytes(levels, n):
+    b = _I32()
+    _check("kvq_fixed_width_container_bytes", lib().kvq_fixed_width_container_bytes(levels, n, ctypes.byref(b)))
+    return b.value
+
+
+def kvq_encode_fixed_width(plan, k, v, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, stream=None):
+    """As kvq_encode_streams, in the fixed-width comparator format."""
+    if k.dtype != v.dtype or k.shape != v.shape:
+        raise ValueError("k and v must have the same dtype and shape")
+    dt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}.get(k.dtype)
+    if dt is None:
+        raise TypeError("k/v must be float32 or bfloat16")
+    S, T = int(k.shape[0]), int(k.shape[1])
+    _check("kvq_encode_fixed_width", lib().kvq_encode_fixed_width(
+        plan.handle, _ptr(k), _ptr(v), dt, S, T, _ptr(k_cont), _ptr(v_cont), _ptr(k_so),
+        _ptr(v_so), _ptr(k_mean_q), _ptr(k_mean_scale), _stream(stream)))
+
+
+def kvq_decode_attention_fixed_width(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, out,
+                                     workspace, out_f32=None, softmax_scale=0.0, stream=None):
+    """As kvq_decode_attention, over fixed-width containers."""
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("q and out must be bfloat16")
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    T = int(k_cont.shape[1])
+    _check("kvq_decode_attention_fixed_width", lib().kvq_decode_attention_fixed_width(
+        plan.handle, _ptr(q), Hq, _ptr(k_cont), _ptr(v_cont), _ptr(k_so), _ptr(v_so),
+        _ptr(k_mean_q), _ptr(k_mean_scale), S, T, float(softmax_scale), _ptr(out), _ptr(out_f32),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def kvq_decode_symbols(plan, side, cont, symbols, end_ok=None, stream=None):

@@ -127,6 +127,45 @@ def run_config(sm, mk, mv, ck, cv, attention=True):
     return out
 
 
+def unpack_fw(cont, levels, n):
+    """Symbols of fixed-width containers (the layout of kvq_encode_fixed_width)."""
+    b = 1
+    while (1 << b) < levels:
+        b *= 2
+    per = 8 // b
+    i = torch.arange(n, device=cont.device)
+    c, r = i // 4, i % 4
+    byte = cont[..., (4 * (c // per) + r)].long()
+    return (byte >> (b * (c % per))) & ((1 << b) - 1)
+
+
+def run_fixed_width(sm, mk=6, mv=3):
+    """The Appendix B comparator on the same sample: NMSE and attention error."""
+    w = sm.w
+    ck, cv = kvq.kvq_fixed_width_container_bytes(mk, w.n), kvq.kvq_fixed_width_container_bytes(mv, w.n)
+    plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4)
+    c = kvq.alloc_cache(plan, sm.S, sm.T)
+    kvq.kvq_encode_fixed_width(plan, sm.k, sm.v, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
+                               c["k_mean_q"], c["k_mean_scale"])
+    out = {"levels": [mk, mv], "containers": [ck, cv], "bits_per_elem": plan.bits_per_elem(True)}
+    mu = (c["k_mean_q"].double() * c["k_mean_scale"].view(torch.float16).double()[..., None])
+    mu_tok = mu.repeat_interleave(128, dim=1)
+    for name, key, so_key, M, ref in (("k", "k_cont", "k_so", mk, sm.k_rot), ("v", "v_cont", "v_so", mv, sm.v_rot)):
+        sym = unpack_fw(c[key], M, w.n).double()
+        so = c[so_key].view(torch.float16).double()
+        rec = so[..., 0:1] * sym + so[..., 1:2] + (mu_tok if name == "k" else 0.0)
+        out[f"nmse_{name}"] = float(((rec - ref) ** 2).sum() / (ref ** 2).sum())
+    o = torch.empty(sm.S, w.n_q_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    o32 = torch.empty_like(o, dtype=torch.float32)
+    ws = torch.empty(plan.workspace_bytes(1, sm.S, sm.T, w.n_q_heads), dtype=torch.uint8, device="cuda")
+    kvq.kvq_decode_attention_fixed_width(plan, sm.q, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
+                                         c["k_mean_q"], c["k_mean_scale"], o, ws, out_f32=o32)
+    err = (o32.double() - sm.exact).norm(dim=-1) / sm.exact.norm(dim=-1)
+    out["attn_rel_err"] = float(err.mean())
+    torch.cuda.synchronize()
+    return out
+
+
 def fmt(x, spec=".4f"):
     return "—" if x is None else format(x, spec)
 
@@ -206,6 +245,18 @@ def main(argv=None):
           f"coding table: K {d['table_gap_k']:.4f}, V {d['table_gap_v']:.4f}")
     print(f"* measured K histogram {d['hist_k']}")
     print(f"* measured V histogram {d['hist_v']}")
+    # Appendix B analogue: the fixed-width comparator at 6/3 levels
+    fw = run_fixed_width(sm)
+    res["fixed_width"] = fw
+    print("\n## Fixed-width comparator, nearest rounding at 6/3 levels (Appendix B analogue)\n")
+    print("| format | levels | bytes K/V | stored bits/value | K NMSE | V NMSE | attention rel. error |")
+    print("|---|---|---|---:|---:|---:|---:|")
+    print(f"| entropy-coded | 8/6 | 331/231 | {d['bits_per_elem']:.3f} | {d['nmse_k']:.4%} | {d['nmse_v']:.4%} | "
+          f"{d['attn_rel_err']:.4%} |")
+    print(f"| fixed width | 6/3 | {fw['containers'][0]}/{fw['containers'][1]} | {fw['bits_per_elem']:.3f} | "
+          f"{fw['nmse_k']:.4%} | {fw['nmse_v']:.4%} | {fw['attn_rel_err']:.4%} |")
+    print("\n(The page charges the fixed-width format the ideal log2 6 + log2 3 bits, i.e. the same "
+          "2.26 bits/value; stored at power-of-two widths it takes the bytes above.)")
     if args.json:
         with open(args.json, "w") as fh:
             json.dump(res, fh, indent=1)

@@ -28,6 +28,8 @@ Modules:
   attention  dequantise-then-attend reference in float64 (plain and factored)
   accounting bits-per-value accounting and the budget -> container helper
   pipeline   whole-cache encode/decode used by the tests and the baseline
+  fixedwidth the fixed-width comparator of Appendix B (nearest rounding,
+             power-of-two symbol widths)
 
 Parity unpinned: none of the functions here lacks a pin; the pins live in
 tests/test_oracle_*.py (marked not-gpu).
@@ -44,6 +46,8 @@ from .attention import (dequantize_f64, attention_plain_f64,
                         attention_factored_f64, attention_with_residual_f64)
 from .accounting import bits_per_elem, containers_for_budget
 from .pipeline import OracleParams, encode_cache, decode_cache_symbols
+from .fixedwidth import (fw_bits, fw_container_bytes, fw_pack, fw_unpack, encode_streams_fw,
+                         encode_cache_fw)
 
 __all__ = [
     "L_RANS", "PROB_BITS", "SIGMA_BITS", "budget_fx", "order_stat_probs", "sharpen",
@@ -54,4 +58,5 @@ __all__ = [
     "rans_encode", "rans_decode", "dequantize_f64", "attention_plain_f64",
     "attention_factored_f64", "attention_with_residual_f64", "bits_per_elem", "containers_for_budget",
     "OracleParams", "encode_cache", "decode_cache_symbols",
+    "fw_bits", "fw_container_bytes", "fw_pack", "fw_unpack", "encode_streams_fw", "encode_cache_fw",
 ]

@@ -134,3 +134,22 @@ def test_model_probs_match_oracle(M, n, alpha):
     p = O.order_stat_probs(M, n)
     want = O.sharpen(p, alpha) if alpha != 1.0 else p
     assert np.max(np.abs(got - want)) <= 1e-9
+
+
+def test_fixed_width_sizes_and_errors():
+    L = _lib()
+    assert kvq.kvq_fixed_width_container_bytes(6, 1024) == 512 == O.fw_container_bytes(6, 1024)
+    assert kvq.kvq_fixed_width_container_bytes(3, 1024) == 256 == O.fw_container_bytes(3, 1024)
+    assert kvq.kvq_fixed_width_container_bytes(2, 1024) == 128
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_fixed_width_container_bytes(6, 4)          # 16 bits: not whole dwords
+    p = ctypes.c_void_p
+    a16 = p(1 << 20)
+    st = p(0)
+    plan = kvq.Plan(8, 128, 6, 3, 331, 231)                # entropy-coded sizes, not fixed-width ones
+    assert L.kvq_encode_fixed_width(plan.handle, a16, a16, 1, 1, 128, a16, a16, a16, a16, a16, a16, st) == -1
+    assert L.kvq_decode_attention_fixed_width(plan.handle, a16, 32, a16, a16, a16, a16, a16, a16, 1, 128, 0.0,
+                                              a16, None, a16, 1 << 30, st) == -1
+    fw = kvq.Plan(8, 128, 16, 3, 512, 256)                 # 16 key levels: no 4-entry level lookup
+    assert L.kvq_decode_attention_fixed_width(fw.handle, a16, 32, a16, a16, a16, a16, a16, a16, 1, 128, 0.0,
+                                              a16, None, a16, 1 << 30, st) == -3
