@@ -37,7 +37,7 @@ tests/test_oracle_*.py (marked not-gpu).
 
 from .model import (L_RANS, PROB_BITS, SIGMA_BITS, budget_fx, order_stat_probs, sharpen,
                     integer_table, build_table, rate_table, lambda_table,
-                    decode_table)
+                    decode_table, level_midpoints, level_values_fp16)
 from .transform import fwht_f32, hadamard_f64, rotate_heads, key_window_mean
 from .quant import (fit_minmax, drift, refit, refit_f64, lane_sum_f64,
                     nearest_levels, encode_streams_alg1)
@@ -51,6 +51,7 @@ from .fixedwidth import (fw_bits, fw_container_bytes, fw_pack, fw_unpack, encode
 
 __all__ = [
     "L_RANS", "PROB_BITS", "SIGMA_BITS", "budget_fx", "order_stat_probs", "sharpen",
+    "level_midpoints", "level_values_fp16",
     "refit_f64", "lane_sum_f64", "nearest_levels",
     "integer_table", "build_table", "rate_table", "lambda_table",
     "decode_table", "fwht_f32", "hadamard_f64", "rotate_heads",

@@ -24,10 +24,12 @@ from .transform import hadamard_f64
 F64 = np.float64
 
 
-def dequantize_f64(sym, so16, mu_hat_tok=None):
-    """s m + o (+ mu) in float64; sym [T, n], so16 float16 [T, 2], mu [T, n]."""
+def dequantize_f64(sym, so16, mu_hat_tok=None, vals=None):
+    """s v_m + o (+ mu) in float64; sym [T, n], so16 float16 [T, 2], mu [T, n];
+    vals are the level values (None: v_m = m)."""
     so = np.asarray(so16, np.float16).astype(F64)
-    out = so[:, 0:1] * np.asarray(sym, F64) + so[:, 1:2]
+    lev = np.asarray(sym, F64) if vals is None else np.asarray(vals, np.float32).astype(F64)[np.asarray(sym)]
+    out = so[:, 0:1] * lev + so[:, 1:2]
     if mu_hat_tok is not None:
         out = out + np.asarray(mu_hat_tok, np.float32).astype(F64)
     return out
@@ -58,8 +60,9 @@ def attention_plain_f64(q, khat_rot, vhat_rot, n_kv_heads, head_dim, scale=None)
 
 
 def attention_factored_f64(q, k_sym, k_so16, mu_hat_tok, v_sym, v_so16,
-                           n_kv_heads, head_dim, scale=None):
-    """Eqs. (8)-(9): contractions on the symbols, affine terms applied after."""
+                           n_kv_heads, head_dim, scale=None, k_vals=None, v_vals=None):
+    """Eqs. (8)-(9): contractions on the decoded levels v_m, affine terms
+    applied after (k_vals / v_vals: level values, None for v_m = m)."""
     q = np.asarray(q, F64)
     Hq, d = q.shape
     T = k_sym.shape[0]
@@ -68,8 +71,10 @@ def attention_factored_f64(q, k_sym, k_so16, mu_hat_tok, v_sym, v_so16,
     H = hadamard_f64(d)
     ks = np.asarray(k_so16, np.float16).astype(F64)
     vs = np.asarray(v_so16, np.float16).astype(F64)
-    km = np.asarray(k_sym, F64).reshape(T, n_kv_heads, d)
-    vm = np.asarray(v_sym, F64).reshape(T, n_kv_heads, d)
+    lev = lambda sym, vals: (np.asarray(sym, F64) if vals is None
+                             else np.asarray(vals, np.float32).astype(F64)[np.asarray(sym)])
+    km = lev(k_sym, k_vals).reshape(T, n_kv_heads, d)
+    vm = lev(v_sym, v_vals).reshape(T, n_kv_heads, d)
     mu = np.asarray(mu_hat_tok, np.float32).astype(F64).reshape(T, n_kv_heads, d)
     out = np.zeros((Hq, d), F64)
     for h in range(Hq):

@@ -9,7 +9,10 @@ Appendix A, Algorithm 1 (r_m = -log2(f_m / sum f)).
 Readings (the page does not spell these out):
   * The model p_m(M, n) is the expected fraction of level m when n iid N(0,1)
     values are min-max normalised (Eq. 4) and rounded to the nearest of the M
-    levels.  The minimum always lands on level 0 and the maximum on level M-1;
+    levels.  Appendix A lets a table entry carry any reconstruction level v_m;
+    with non-affine levels (v_0 = 0 < ... < v_{M-1} = M - 1 in grid units) the
+    cells of nearest rounding are bounded by the midpoints of adjacent levels,
+    and the model is symmetrised only when the levels are symmetric.  The minimum always lands on level 0 and the maximum on level M-1;
     the other n-2 values are iid N(0,1) truncated to (min, max).  It is
     evaluated by 2-D Gauss-Legendre quadrature in float64 and symmetrised
     (p_m and p_{M-1-m} are equal by symmetry of the normal law; averaging them
@@ -33,10 +36,30 @@ L_RANS = 1 << 23              # lower end of the normalised state interval
 RATE_FRAC_BITS = 16
 
 
-def order_stat_probs(M, n, nodes=512, lo=-9.0, hi=9.0):
-    """p_m(M, n) in float64 (see module docstring), symmetrised."""
+def level_midpoints(M, values=None):
+    """Cell boundaries, in grid units, of nearest rounding to the M levels:
+    (v_{m-1} + v_m) / 2 for m = 1..M-1 (affine levels v_m = m give m - 1/2)."""
+    if values is None:
+        return np.arange(1, M, dtype=np.float64) - 0.5
+    v = np.asarray(values, np.float64)
+    return 0.5 * (v[:-1] + v[1:])
+
+
+def levels_symmetric(M, values=None):
+    """True if v_m + v_{M-1-m} == M - 1 exactly for every m."""
+    if values is None:
+        return True
+    v = np.asarray(values, np.float64)
+    return bool(np.all(v + v[::-1] == float(M - 1)))
+
+
+def order_stat_probs(M, n, nodes=512, lo=-9.0, hi=9.0, values=None):
+    """p_m(M, n) in float64 (see module docstring), symmetrised when the
+    levels are.  ``values`` are non-affine level positions in grid units
+    (v_0 = 0, v_{M-1} = M - 1, increasing); None means v_m = m."""
     if M < 2 or n < 2:
         raise ValueError("need M >= 2 and n >= 2")
+    mids = level_midpoints(M, values)
     p = np.zeros(M, np.float64)
     p[0] += 1.0
     p[M - 1] += 1.0
@@ -58,15 +81,34 @@ def order_stat_probs(M, n, nodes=512, lo=-9.0, hi=9.0):
         wts = wa[:, None] * wb * dens
         width = b - A
         for m in range(M):
-            e_lo = np.clip(A + width * ((m - 0.5) / (M - 1)), A, b)
-            e_hi = np.clip(A + width * ((m + 0.5) / (M - 1)), A, b)
+            lo_u = mids[m - 1] if m > 0 else -0.5
+            hi_u = mids[m] if m < M - 1 else M - 0.5
+            e_lo = np.clip(A + width * (lo_u / (M - 1)), A, b)
+            e_hi = np.clip(A + width * (hi_u / (M - 1)), A, b)
             cell = special.ndtr(e_hi) - special.ndtr(e_lo)
             p[m] += float(n - 2) * float(np.sum(wts * cell))
     p /= float(n)
+    if not levels_symmetric(M, values):
+        return p
     sym = np.empty_like(p)
     for m in range(M):
         sym[m] = (p[m] + p[M - 1 - m]) / 2.0
     return sym
+
+
+def level_values_fp16(M, values=None):
+    """The reconstruction levels as stored in the table: float16, returned as
+    float32 (v_m = m when values is None).  Raises unless v_0 = 0,
+    v_{M-1} = M - 1 and the levels strictly increase after rounding."""
+    if values is None:
+        return np.arange(M, dtype=np.float32)
+    v = np.asarray(values, np.float64)
+    if v.shape != (M,):
+        raise ValueError("need one value per level")
+    v16 = v.astype(np.float32).astype(np.float16).astype(np.float32)
+    if v16[0] != 0.0 or v16[-1] != float(M - 1) or not np.all(np.diff(v16) > 0):
+        raise ValueError("levels must rise strictly from 0 to M - 1")
+    return v16
 
 
 def sharpen(p, alpha):
@@ -98,9 +140,9 @@ def integer_table(q, total=1 << PROB_BITS):
     return f
 
 
-def build_table(M, n, alpha):
+def build_table(M, n, alpha, values=None):
     """(f, c): frequencies and cumulative frequencies in symbol order."""
-    f = integer_table(sharpen(order_stat_probs(M, n), alpha))
+    f = integer_table(sharpen(order_stat_probs(M, n, values=values), alpha))
     c = np.zeros(M, np.int64)
     for m in range(1, M):
         c[m] = c[m - 1] + f[m - 1]

@@ -13,7 +13,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .model import build_table, rate_table, lambda_table, budget_fx
+from .model import build_table, rate_table, lambda_table, budget_fx, level_values_fp16
 from .transform import rotate_heads, key_window_mean
 from .quant import encode_streams_alg1
 from .rans import rans_decode
@@ -31,17 +31,26 @@ class OracleParams:
     container_bytes_v: int = 231
     mean_window: int = 128
     alpha: float = 1.4
+    values_k: tuple = None        # non-affine key levels in grid units (None: v_m = m)
+    values_v: tuple = None
     _cache: dict = field(default_factory=dict, repr=False, compare=False)
 
     @property
     def n(self):
         return self.n_kv_heads * self.head_dim
 
+    def vals(self, side):
+        """Level values as stored (float16, as float32)."""
+        M = self.levels_k if side == "k" else self.levels_v
+        return level_values_fp16(M, self.values_k if side == "k" else self.values_v)
+
     def table(self, side):
         """(f, c, r_fx) for side 'k' or 'v'."""
         if side not in self._cache:
             M = self.levels_k if side == "k" else self.levels_v
-            f, c = build_table(M, self.n, self.alpha)
+            raw = self.values_k if side == "k" else self.values_v
+            vals = None if raw is None else self.vals(side).astype(float)
+            f, c = build_table(M, self.n, self.alpha, vals)
             self._cache[side] = (f, c, rate_table(f))
         return self._cache[side]
 
@@ -57,9 +66,9 @@ class OracleParams:
                 raise ValueError(f"container too small for side {side}")
 
 
-def _encode_side(x, levels, tab, C, E, chunk):
+def _encode_side(x, levels, tab, C, E, chunk, vals=None):
     f, c, r = tab
-    outs = [encode_streams_alg1(x[i:i + chunk], levels, f, c, r, C, E)
+    outs = [encode_streams_alg1(x[i:i + chunk], levels, f, c, r, C, E, vals)
             for i in range(0, x.shape[0], chunk)]
     cat = lambda k: np.concatenate([o[k] for o in outs])
     return {
@@ -82,8 +91,10 @@ def encode_cache(k, v, p, chunk=256):
     mu_q, mu_sc, mu_hat = key_window_mean(k_rot, p.mean_window)
     xk = k_rot - np.repeat(mu_hat, p.mean_window, axis=0)
     E = p.lam()
-    ks = _encode_side(xk, p.levels_k, p.table("k"), p.container_bytes_k, E, chunk)
-    vs = _encode_side(v_rot, p.levels_v, p.table("v"), p.container_bytes_v, E, chunk)
+    vk = None if p.values_k is None else p.vals("k")
+    vv = None if p.values_v is None else p.vals("v")
+    ks = _encode_side(xk, p.levels_k, p.table("k"), p.container_bytes_k, E, chunk, vk)
+    vs = _encode_side(v_rot, p.levels_v, p.table("v"), p.container_bytes_v, E, chunk, vv)
     return {
         "k_cont": ks["cont"], "v_cont": vs["cont"],
         "k_so": ks["so"], "v_so": vs["so"],

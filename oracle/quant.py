@@ -23,13 +23,13 @@ Readings (the page leaves the arithmetic open; these fix it):
   * If no tested lambda was feasible the assignment at 2^hi is evaluated; if
     that is infeasible too, every symbol takes the cheapest level (a
     "fallback"; the plan guarantees n * min r_fx <= B_fx, so it always fits).
-  * Refit: least squares of x on [1, m] in float64.  S1 = sum m, S2 = sum m^2
-    are exact integers; Sx = sum x_i and Smx = sum m_i x_i are float64 sums in
-    a fixed order: the n values are split into 64 contiguous chunks of
+  * Refit: least squares of x on [1, v_m] in float64 (v_m = m for affine
+    levels).  S1 = sum v_m, S2 = sum v_m^2, Sx = sum x_i and Smx = sum v_m x_i
+    are float64 sums in a fixed order (S1, S2 are exact for affine levels): the n values are split into 64 contiguous chunks of
     ceil(n/64) (chunk l holds i in [l q, (l+1) q)), each chunk is summed from
     +0.0 in increasing i, and the 64 partial sums are combined by six
     butterfly rounds p_l <- p_l + p_(l xor k), k = 32, 16, 8, 4, 2, 1.
-    den = n S2 - S1^2; if den == 0 then s' = s, o' = (Sx - s S1) / n, else
+    den = RN(n S2) - RN(S1 S1); if den == 0 then s' = s, o' = (Sx - s S1) / n, else
     s' = (n Smx - S1 Sx) / den, o' = (Sx - s' S1) / n (each step one float64
     operation).  If s' < 0 or anything is not finite, (s', o') = (s, o).
     The stored metadata is fp16(fp32(s')), fp16(fp32(o')).
@@ -59,8 +59,8 @@ def fit_minmax(x, levels):
     return s.astype(F32), mn.astype(F32)
 
 
-def _distortion(x, s, o, levels):
-    lev = np.arange(levels, dtype=F32)
+def _distortion(x, s, o, levels, vals=None):
+    lev = np.arange(levels, dtype=F32) if vals is None else np.asarray(vals, F32)
     rec = o[:, None] + s[:, None] * lev[None, :]
     delta = x[:, :, None] - rec[:, None, :]
     return delta * delta                                  # [N, n, M] float32
@@ -75,11 +75,13 @@ def _assign(D, rate_f32, r_fx, u, E):
     return m, r_fx[m].sum(axis=1)
 
 
-def drift(x, s, o, r_fx, B_fx, E, trace=None):
+def drift(x, s, o, r_fx, B_fx, E, trace=None, vals=None):
     """Drift(x, s, o, r, B) of Algorithm 1 for every row of x.
 
     B_fx is the budget in rate fixed point (``model.budget_fx(C)``).  If
     ``trace`` is a list, the lambda grid point of every evaluation is appended.
+    ``vals`` are the level values (float32; None: v_m = m), so that
+    rec_m = RN(o + RN(s v_m)).
     Returns (m [N, n] int64, fallback [N] bool)."""
     x = np.asarray(x, F32)
     s = np.asarray(s, F32)
@@ -89,7 +91,7 @@ def drift(x, s, o, r_fx, B_fx, E, trace=None):
     M = len(r_fx)
     rate_f32 = (r_fx.astype(F64) / float(1 << RATE_FRAC_BITS)).astype(F32)
     m_star = int(np.argmin(r_fx))
-    D = _distortion(x, s, o, M)
+    D = _distortion(x, s, o, M, vals)
     y = (D.max(axis=(1, 2)) - D.min(axis=(1, 2))) * F32(8)
     if not np.all(np.isfinite(y)):
         raise ValueError("distortion range is not finite")
@@ -143,21 +145,25 @@ def lane_sum_f64(v):
     return p[:, 0]
 
 
-def refit_f64(x, m, s, o):
-    """Least-squares (s', o') of x on [1, m] in float64, with the guard."""
+def refit_f64(x, m, s, o, vals=None):
+    """Least-squares (s', o') of x on [1, v_m] in float64, with the guard.
+
+    The level sums S1 = sum v_m, S2 = sum v_m^2 use the same fixed order as the
+    other sums; with affine levels they are exact integers, and so is
+    den = RN(n S2) - RN(S1 S1) (below 2^53)."""
     x = np.asarray(x, F32)
     m = np.asarray(m, np.int64)
     N, n = x.shape
-    S1 = m.sum(axis=1)
-    S2 = (m * m).sum(axis=1)
+    vd = (m.astype(F64) if vals is None else np.asarray(vals, F32).astype(F64)[m])
+    S1d = lane_sum_f64(vd)
+    S2d = lane_sum_f64(vd * vd)
     xd = x.astype(F64)
     Sx = lane_sum_f64(xd)
-    Smx = lane_sum_f64(m.astype(F64) * xd)
-    den = n * S2 - S1 * S1
+    Smx = lane_sum_f64(vd * xd)
+    nd = F64(n)
+    den = nd * S2d - S1d * S1d
     s64 = np.asarray(s, F32).astype(F64)
     o64 = np.asarray(o, F32).astype(F64)
-    S1d = S1.astype(F64)
-    nd = F64(n)
     with np.errstate(all="ignore"):
         flat = den == 0
         den_d = np.where(flat, 1, den).astype(F64)
@@ -167,11 +173,11 @@ def refit_f64(x, m, s, o):
     return np.where(bad, s64, s_new), np.where(bad, o64, o_new)
 
 
-def refit(x, m, s, o):
+def refit(x, m, s, o, vals=None):
     """Refit (s, o) to the assignment m, then round to fp16 via fp32.
 
     Returns (s16, o16) as float16 arrays."""
-    s_new, o_new = refit_f64(x, m, s, o)
+    s_new, o_new = refit_f64(x, m, s, o, vals)
     with np.errstate(over="ignore"):
         s16 = s_new.astype(F32).astype(np.float16)
         o16 = o_new.astype(F32).astype(np.float16)
@@ -180,13 +186,13 @@ def refit(x, m, s, o):
     return s16, o16
 
 
-def nearest_levels(x, s, o, levels):
+def nearest_levels(x, s, o, levels, vals=None):
     """argmin_m D_im (lowest index on ties): the lambda -> 0 assignment."""
-    D = _distortion(np.asarray(x, F32), np.asarray(s, F32), np.asarray(o, F32), levels)
+    D = _distortion(np.asarray(x, F32), np.asarray(s, F32), np.asarray(o, F32), levels, vals)
     return np.argmin(D, axis=2)
 
 
-def encode_streams_alg1(x, levels, f, c, r_fx, container_bytes, E):
+def encode_streams_alg1(x, levels, f, c, r_fx, container_bytes, E, vals=None):
     """Algorithm 1 for each row of x (already rotated and, for keys, centred).
 
     Returns a dict with the containers [N, C] (uint8), s16/o16 (float16 [N]),
@@ -196,12 +202,12 @@ def encode_streams_alg1(x, levels, f, c, r_fx, container_bytes, E):
     x = np.asarray(x, F32)
     s, o = fit_minmax(x, levels)
     B_fx = budget_fx(container_bytes)
-    m1, fb1 = drift(x, s, o, r_fx, B_fx, E)
-    s16, o16 = refit(x, m1, s, o)
+    m1, fb1 = drift(x, s, o, r_fx, B_fx, E, vals=vals)
+    s16, o16 = refit(x, m1, s, o, vals)
     s2 = s16.astype(F32)
     o2 = o16.astype(F32)
-    m2, fb2 = drift(x, s2, o2, r_fx, B_fx, E)
+    m2, fb2 = drift(x, s2, o2, r_fx, B_fx, E, vals=vals)
     cont, k = rans_encode(m2, f, c, container_bytes)
-    changed = int((nearest_levels(x, s2, o2, levels) != m2).sum())
+    changed = int((nearest_levels(x, s2, o2, levels, vals) != m2).sum())
     return {"cont": cont, "s16": s16, "o16": o16, "m": m2, "payload": k,
             "fallback1": fb1, "fallback2": fb2, "changed": changed}
