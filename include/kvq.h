@@ -72,6 +72,23 @@ typedef struct kvq_plan kvq_plan;
 kvq_status kvq_plan_create(const kvq_params* params, kvq_plan** out_plan);
 void kvq_plan_destroy(kvq_plan* plan);
 
+/* As kvq_plan_create, with non-affine reconstruction levels ([D-Quant]
+ * Appendix A: a table entry carries the level v_m; Eqs. (7)-(9) hold for any
+ * v_m).  values_k / values_v (nullable: v_m = m) hold levels_k / levels_v
+ * levels in grid units; they are rounded to fp16, which is what is stored,
+ * and must then rise strictly from 0 to levels - 1 (KVQ_EINVAL otherwise), so
+ * the min-max fit of Eq. 4 is unchanged.  Nearest rounding, drift and the
+ * least-squares refit use rec_m = o + s v_m, and the probability model's cells
+ * are bounded by the midpoints of adjacent levels (symmetrised only for
+ * symmetric levels).  Decode attention accepts non-affine plans when both
+ * alphabets have at most 16 (keys) and 8 (values) levels; the fixed-width
+ * comparator needs affine levels. */
+kvq_status kvq_plan_create_levels(const kvq_params* params, const float* values_k,
+                                  const float* values_v, kvq_plan** out_plan);
+
+/* Copies one side's level values v_m as stored (16 floats; zero past levels). */
+kvq_status kvq_plan_levels(const kvq_plan* plan, int side, float* values);
+
 /* Copies one side's tables (side 0 = keys, 1 = values) to host arrays of at
  * least 16 entries: frequencies f_m (sum 256), cumulative c_m and the rates
  * r_fx[m] = rne((8 - log2 f_m) * 2^16).  Entries >= levels are zero. */

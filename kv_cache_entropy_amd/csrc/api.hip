@@ -71,6 +71,7 @@ kvq::EncTabs enc_tabs(const kvq_plan* plan, int side) {
     e.cum[m] = t.cum[m];
     e.rcp[m] = t.rcp[m];
     e.rshift[m] = t.rshift[m];
+    e.level[m] = t.level[m];
   }
   std::memcpy(e.lambda, plan->lambda_grid, sizeof(e.lambda));
   e.levels = t.levels;
@@ -190,6 +191,7 @@ kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_d
   if (n % 64 || n > 4096 || W < 4) return KVQ_EUNSUPPORTED;
   int fwb[2] = {0, 0};
   if (fixed_width) {
+    if (!plan->side[0].affine || !plan->side[1].affine) return KVQ_EUNSUPPORTED;
     fwb[0] = fw_bits(P.levels_k);
     fwb[1] = fw_bits(P.levels_v);
     for (int side = 0; side < 2; ++side) {
@@ -276,11 +278,13 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
   }
   const int G = n_q_heads / Hkv;
   const int bk = fw_bits(P.levels_k), bv = fw_bits(P.levels_v);
+  const bool affine = plan->side[0].affine && plan->side[1].affine;
   if (fixed_width) {
     if (P.container_bytes_k != plan->n * bk / 8 || P.container_bytes_v != plan->n * bv / 8) return KVQ_EINVAL;
+    if (!affine) return KVQ_EUNSUPPORTED;
     if (n_tokens % 64 || W < 64 || !kvq::attention_fw_supported(n_q_heads, G, d, bk, bv, P.levels_k, P.levels_v))
       return KVQ_EUNSUPPORTED;
-  } else if (n_tokens % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W)) {
+  } else if (n_tokens % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W, affine)) {
     return KVQ_EUNSUPPORTED;
   }
   if (n_seqs > 65535) return KVQ_EUNSUPPORTED;
@@ -349,6 +353,9 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
       aa.fv[m] = plan->side[1].freq[m];
       aa.cv[m] = plan->side[1].cum[m];
       aa.hbv[m] = plan->side[1].fp16_hi[m];
+      aa.lvk[m] = plan->side[0].fp16_bits[m];
+      aa.lbv[m] = plan->side[1].fp16_lo[m];
+      if (aa.lbv[m]) aa.v_lo_nonzero = 1;
     }
     size_t slot = 0;
     const bool timed = timer_begin(stream, &slot);

@@ -603,6 +603,31 @@ __device__ inline uint32_t dec5_step(uint32_t& x, uint32_t win, uint32_t& sel, c
   return e;
 }
 
+// PV over the 64 tokens of a tile for 64 channels: the int8 level indices of
+// the [channel][token] chunk become fp16 through v_perm lookups (high bytes;
+// with LO also the low bytes of non-integer levels) and are contracted on
+// 4x4x4 MFMA blocks with the softmax weights (hi + lo parts) as A.
+template <int NGM, bool LO>
+__device__ inline void pv_half(const uint8_t* vch, int lane, int qn, const uint16_t* wv, const uint16_t* wv_lo,
+                               uint32_t lutHi, uint32_t lutLo, uint32_t lutHi2, uint32_t lutLo2,
+                               float4_t (&O)[NGM]) {
+#pragma unroll 2
+  for (int tq = 0; tq < 16; ++tq) {
+    const uint32_t idx = *reinterpret_cast<const uint32_t*>(vch + lane * kChunk8Stride + 4 * tq);
+    const uint32_t hb = __builtin_amdgcn_perm(lutHi, lutLo, idx);
+    const uint32_t lb = LO ? __builtin_amdgcn_perm(lutHi2, lutLo2, idx) : 0u;
+    const half4_t B = as_half4(__builtin_amdgcn_perm(hb, lb, 0x05010400u),
+                               __builtin_amdgcn_perm(hb, lb, 0x07030602u));
+#pragma unroll
+    for (int m = 0; m < NGM; ++m) {
+      const uint2 ah = *reinterpret_cast<const uint2*>(wv + (m * 4 + qn) * 64 + 4 * tq);
+      const uint2 al = *reinterpret_cast<const uint2*>(wv_lo + (m * 4 + qn) * 64 + 4 * tq);
+      O[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah.x, ah.y), B, O[m], 0, 0, 0);
+      O[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[m], 0, 0, 0);
+    }
+  }
+}
+
 template <int G, int HKV>
 __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a, int64_t S) {
   using Lay = Lay4<G, HKV>;
@@ -621,7 +646,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
     uint32_t mk = 0, mv = 0;
     for (int m = 1; m < a.Mk; ++m) mk = (z >= a.ck[m]) ? uint32_t(m) : mk;
     for (int m = 1; m < a.Mv; ++m) mv = (z >= a.cv[m]) ? uint32_t(m) : mv;
-    reinterpret_cast<uint32_t*>(lds + Lay::TABK)[idx] = a.fk[mk] | ((z - a.ck[mk]) << 8) | (a.hbk[mk] << 24);
+    reinterpret_cast<uint32_t*>(lds + Lay::TABK)[idx] = a.fk[mk] | ((z - a.ck[mk]) << 8) | (a.lvk[mk] << 16);
     reinterpret_cast<uint32_t*>(lds + Lay::TABV)[idx] = a.fv[mv] | ((z - a.cv[mv]) << 8) | (mv << 16);
   }
   __syncthreads();
@@ -657,6 +682,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   // fp16 high bytes of V levels 0..7 as a v_perm lookup (low byte is zero)
   const uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
   const uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
+  // low bytes of non-integer value levels (all zero for integer levels)
+  const uint32_t lutLo2 = a.lbv[0] | (a.lbv[1] << 8) | (a.lbv[2] << 16) | (a.lbv[3] << 24);
+  const uint32_t lutHi2 = a.lbv[4] | (a.lbv[5] << 8) | (a.lbv[6] << 16) | (a.lbv[7] << 24);
 
   float4_t O[HKV][2][NGM];
 #pragma unroll
@@ -767,20 +795,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
         }
         // PV of V's head for the 64 channels of this half
         wave_lds_fence();
-#pragma unroll 2
-        for (int tq = 0; tq < 16; ++tq) {
-          const uint32_t idx = *reinterpret_cast<const uint32_t*>(vch + lane * kChunk8Stride + 4 * tq);
-          const uint32_t hb = __builtin_amdgcn_perm(lutHi, lutLo, idx);
-          const half4_t B = as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu),
-                                     __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
-#pragma unroll
-          for (int m = 0; m < NGM; ++m) {
-            const uint2 ah = *reinterpret_cast<const uint2*>(wv + (m * 4 + qn) * 64 + 4 * tq);
-            const uint2 al = *reinterpret_cast<const uint2*>(wv_lo + (m * 4 + qn) * 64 + 4 * tq);
-            O[vg][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah.x, ah.y), B, O[vg][ch][m], 0, 0, 0);
-            O[vg][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[vg][ch][m], 0, 0, 0);
-          }
-        }
+        if (a.v_lo_nonzero)
+          pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[vg][ch]);
+        else
+          pv_half<NGM, false>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, 0u, 0u, O[vg][ch]);
         wave_lds_fence();
       }
       // ---- K head g done: logits -> online softmax -> weights for the next iteration
@@ -1049,11 +1067,15 @@ hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t strea
   return hipGetLastError();
 }
 
-bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int window) {
+bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int window, bool affine) {
   const int hkv = Hq / G;
   const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
   const bool h_ok = hkv == 1 || hkv == 2 || hkv == 4 || hkv == 8;
-  return d == kD && g_ok && h_ok && levels_k <= 9 && levels_v <= 9 && window >= 64;
+  if (d != kD || !g_ok || !h_ok || window < 64) return false;
+  // the eight-wave kernel takes any key levels and up to 8 value levels; the
+  // single-wave one (9 value levels) needs integer levels
+  if (levels_v <= 8) return true;
+  return affine && levels_k <= 9 && levels_v <= 9;
 }
 
 template <int G, int HKV>

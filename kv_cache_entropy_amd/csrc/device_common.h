@@ -28,6 +28,7 @@ struct EncTabs {
   uint32_t cum[kMaxLevels];
   uint32_t rcp[kMaxLevels];
   uint32_t rshift[kMaxLevels];
+  float level[kMaxLevels];     // reconstruction levels v_m (grid units)
   float lambda[kLambdaGrid];
   int levels;
   int container_bytes;
@@ -56,6 +57,7 @@ struct EncodeArgs {
 
 struct EncShared {
   float lambda[kLambdaGrid];
+  float level[kMaxLevels];
   uint32_t rate_fx[kMaxLevels];
   float rate_f[kMaxLevels];
   uint32_t freq[kMaxLevels];
@@ -110,6 +112,9 @@ struct Attn2Args {
   int Mk, Mv;
   uint32_t fk[kMaxLevels], ck[kMaxLevels], hbk[kMaxLevels];
   uint32_t fv[kMaxLevels], cv[kMaxLevels], hbv[kMaxLevels];
+  uint32_t lvk[kMaxLevels];   // fp16 bits of the key levels
+  uint32_t lbv[kMaxLevels];   // low bytes of the fp16 value levels (0 when affine)
+  int v_lo_nonzero;           // some value level has a nonzero low byte
 };
 
 // The uncompressed tail of every sequence (the most recent tokens, kept in
@@ -237,7 +242,7 @@ hipError_t launch_encode(const EncodeArgs& a, int64_t n_streams, hipStream_t str
 hipError_t launch_decode_symbols(const DecSymArgs& a, hipStream_t stream);
 hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t stream);
 hipError_t launch_attention2(const Attn2Args& a, int64_t S, int Hq, int G, hipStream_t stream);
-bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int window);
+bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int window, bool affine);
 hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream);
 hipError_t launch_residual(const ResidualArgs& a, int64_t S, hipStream_t stream);
 bool attention_fw_supported(int Hq, int G, int d, int bk, int bv, int levels_k, int levels_v);

@@ -93,7 +93,7 @@ __device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& 
 #pragma unroll
   for (int i = 0; i < NPL; ++i) { bestD[i] = __builtin_inff(); bl[i] = 0; }
   for (int l = 0; l < levels; ++l) {
-    const float rec = __fadd_rn(o, __fmul_rn(s, float(l)));
+    const float rec = __fadd_rn(o, __fmul_rn(s, sh.level[l]));
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
       const float dl = __fsub_rn(x[i], rec);
@@ -137,7 +137,7 @@ __device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& 
 #pragma unroll
     for (int i = 0; i < NPL; ++i) { best[i] = __builtin_inff(); cur[i] = 0; }
     for (int l = 0; l < levels; ++l) {
-      const float rec = __fadd_rn(o, __fmul_rn(s, float(l)));
+      const float rec = __fadd_rn(o, __fmul_rn(s, sh.level[l]));
       const float lr = __fmul_rn(lam, sh.rate_f[l]);
 #pragma unroll
       for (int i = 0; i < NPL; ++i) {
@@ -172,12 +172,13 @@ __device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& 
 // Nearest level of every value (lowest index on ties): the lambda -> 0
 // assignment, used alone by the fixed-width comparator.
 template <int NPL>
-__device__ void nearest(const float (&x)[NPL], float s, float o, int levels, uint8_t (&m)[NPL]) {
+__device__ void nearest(const float (&x)[NPL], float s, float o, int levels, const float* lev,
+                        uint8_t (&m)[NPL]) {
   float bestD[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) { bestD[i] = __builtin_inff(); m[i] = 0; }
   for (int l = 0; l < levels; ++l) {
-    const float rec = __fadd_rn(o, __fmul_rn(s, float(l)));
+    const float rec = __fadd_rn(o, __fmul_rn(s, lev[l]));
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
       const float dl = __fsub_rn(x[i], rec);
@@ -210,37 +211,38 @@ __device__ void fw_pack_lane(const uint8_t (&m)[NPL], uint32_t* img_words, int l
   }
 }
 
-// Least-squares refit in float64 with the fixed summation order (chunk per
-// lane in increasing index from +0, then xor-butterfly 32..1), the guard, and
-// rounding to fp16 through fp32.
+// Least-squares refit on [1, v_m] in float64 with the fixed summation order
+// (chunk per lane in increasing index from +0, then xor-butterfly 32..1) for
+// every sum, the guard, and rounding to fp16 through fp32.  With affine levels
+// the level sums and den are exact integers.
 template <int NPL>
 __device__ void refit(const float (&x)[NPL], const uint8_t (&m)[NPL], float s, float o, int n,
-                      __half& s16, __half& o16) {
-  double px = 0.0, pmx = 0.0;
-  int s1 = 0, s2 = 0;
+                      const float* lev, __half& s16, __half& o16) {
+  double px = 0.0, pmx = 0.0, p1 = 0.0, p2 = 0.0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const double xd = double(x[i]);
+    const double vd = double(lev[m[i]]);
     px = __dadd_rn(px, xd);
-    pmx = __dadd_rn(pmx, __dmul_rn(double(m[i]), xd));
-    s1 += m[i];
-    s2 += int(m[i]) * int(m[i]);
+    pmx = __dadd_rn(pmx, __dmul_rn(vd, xd));
+    p1 = __dadd_rn(p1, vd);
+    p2 = __dadd_rn(p2, __dmul_rn(vd, vd));
   }
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) {
     px = __dadd_rn(px, __shfl_xor(px, k, 64));
     pmx = __dadd_rn(pmx, __shfl_xor(pmx, k, 64));
+    p1 = __dadd_rn(p1, __shfl_xor(p1, k, 64));
+    p2 = __dadd_rn(p2, __shfl_xor(p2, k, 64));
   }
-  const int64_t S1 = wave_sum_i32(s1);
-  const int64_t S2 = wave_sum_i32(s2);
-  const int64_t den = int64_t(n) * S2 - S1 * S1;
-  const double S1d = double(S1), nd = double(n);
+  const double nd = double(n), S1d = p1;
+  const double den = __dsub_rn(__dmul_rn(nd, p2), __dmul_rn(S1d, S1d));
   double sn, on;
-  if (den == 0) {
+  if (den == 0.0) {
     sn = double(s);
     on = __ddiv_rn(__dsub_rn(px, __dmul_rn(sn, S1d)), nd);
   } else {
-    sn = __ddiv_rn(__dsub_rn(__dmul_rn(nd, pmx), __dmul_rn(S1d, px)), double(den));
+    sn = __ddiv_rn(__dsub_rn(__dmul_rn(nd, pmx), __dmul_rn(S1d, px)), den);
     on = __ddiv_rn(__dsub_rn(px, __dmul_rn(sn, S1d)), nd);
   }
   if (!(sn >= 0.0) || !isfinite(sn) || !isfinite(on)) {
@@ -300,6 +302,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   uint8_t* img = dyn + size_t(SPW) * n;    // [SPW][C]
   for (int i = tid; i < 512; i += 256) sh.lambda[i] = a.tabs.lambda[i];
   if (tid < kMaxLevels) {
+    sh.level[tid] = a.tabs.level[tid];
     sh.rate_fx[tid] = a.tabs.rate_fx[tid];
     sh.rate_f[tid] = float(a.tabs.rate_fx[tid]) * (1.0f / 65536.0f);
     sh.freq[tid] = a.tabs.freq[tid];
@@ -339,13 +342,13 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     uint8_t m[NPL];
     __half s16, o16;
     if constexpr (FW) {
-      nearest<NPL>(x, s, o, M, m);
-      refit<NPL>(x, m, s, o, n, s16, o16);
-      nearest<NPL>(x, __half2float(s16), __half2float(o16), M, m);
+      nearest<NPL>(x, s, o, M, sh.level, m);
+      refit<NPL>(x, m, s, o, n, sh.level, s16, o16);
+      nearest<NPL>(x, __half2float(s16), __half2float(o16), M, sh.level, m);
       if constexpr (FW) fw_pack_lane<NPL, FWB>(m, reinterpret_cast<uint32_t*>(img + size_t(sl) * C), lane);
     } else {
       fb1 += drift<NPL>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
-      refit<NPL>(x, m, s, o, n, s16, o16);
+      refit<NPL>(x, m, s, o, n, sh.level, s16, o16);
       uint8_t near[NPL];
       fb2 += drift<NPL>(x, __half2float(s16), __half2float(o16), sh, M, m, &near) ? 1u : 0u;
       uint32_t ch = 0;

@@ -27,7 +27,11 @@ struct SideTables {
   uint32_t rcp[kMaxLevels];
   uint32_t rshift[kMaxLevels];
   uint32_t dec[256];
-  uint32_t fp16_hi[kMaxLevels];  // high byte of fp16(level); its low byte is 0 for levels <= 8
+  uint32_t fp16_hi[kMaxLevels];  // high byte of fp16(v_m)
+  uint32_t fp16_lo[kMaxLevels];  // low byte of fp16(v_m) (0 for integer levels <= 8)
+  uint32_t fp16_bits[kMaxLevels];
+  float level[kMaxLevels];       // v_m as stored (fp16), in grid units
+  int affine;                    // v_m == m for every m
   uint32_t cheapest;   // lowest index with the smallest rate
   uint64_t budget_fx;  // (8C - 32) * 2^16
 };

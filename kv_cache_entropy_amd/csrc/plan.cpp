@@ -56,8 +56,54 @@ void gauss_legendre(int N, std::vector<double>& x, std::vector<double>& w) {
 double Phi(double v) { return 0.5 * std::erfc(-v / std::sqrt(2.0)); }
 double phi(double v) { return std::exp(-0.5 * v * v) / std::sqrt(2.0 * std::acos(-1.0)); }
 
-// p_m(M, n), symmetrised (p_m = p_{M-1-m} holds exactly for the normal law).
-std::vector<double> order_stat_probs(int M, int n) {
+// IEEE binary16 of a float, round to nearest even (subnormals kept).
+uint16_t f32_to_f16(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const int exp = int((x >> 23) & 0xFFu);
+  uint32_t mant = x & 0x7FFFFFu;
+  if (exp == 0xFF) return uint16_t(sign | 0x7C00u | (mant ? 0x200u : 0u));
+  const int e = exp - 127 + 15;
+  if (e >= 31) return uint16_t(sign | 0x7C00u);
+  if (e <= 0) {
+    if (e < -10) return uint16_t(sign);
+    mant |= 0x800000u;
+    const int shift = 14 - e;
+    uint32_t h = mant >> shift;
+    const uint32_t rem = mant & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (h & 1u))) ++h;
+    return uint16_t(sign | h);
+  }
+  uint32_t h = (uint32_t(e) << 10) | (mant >> 13);
+  const uint32_t rem = mant & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ++h;
+  return uint16_t(sign | h);
+}
+
+float f16_to_f32(uint16_t h) {
+  const uint32_t sign = uint32_t(h & 0x8000u) << 16;
+  const int exp = (h >> 10) & 0x1F;
+  const uint32_t mant = h & 0x3FFu;
+  float v;
+  if (exp == 0) {
+    v = std::ldexp(float(mant), -24);
+  } else if (exp == 31) {
+    v = mant ? std::nanf("") : INFINITY;
+  } else {
+    v = std::ldexp(float(mant | 0x400u), exp - 25);
+  }
+  uint32_t b;
+  std::memcpy(&b, &v, 4);
+  b |= sign;
+  std::memcpy(&v, &b, 4);
+  return v;
+}
+
+// p_m(M, n).  mids[m] (m = 0..M-2) bound the nearest-rounding cells in grid
+// units ((v_m + v_{m+1}) / 2; m + 1/2 for affine levels).  Symmetrised when the
+// levels are symmetric (then p_m = p_{M-1-m} holds exactly for the normal law).
+std::vector<double> order_stat_probs(int M, int n, const std::vector<double>& mids, bool symmetric) {
   std::vector<double> p(M, 0.0);
   p[0] += 1.0;
   p[M - 1] += 1.0;
@@ -80,8 +126,10 @@ std::vector<double> order_stat_probs(int M, int n) {
         if (wt == 0.0) continue;
         const double width = b - a;
         for (int m = 0; m < M; ++m) {
-          double lo = a + width * ((m - 0.5) / (M - 1));
-          double hi = a + width * ((m + 0.5) / (M - 1));
+          const double lo_u = m > 0 ? mids[m - 1] : -0.5;
+          const double hi_u = m < M - 1 ? mids[m] : M - 0.5;
+          double lo = a + width * (lo_u / (M - 1));
+          double hi = a + width * (hi_u / (M - 1));
           lo = std::min(std::max(lo, a), b);
           hi = std::min(std::max(hi, a), b);
           acc[m] += wt * (Phi(hi) - Phi(lo));
@@ -91,6 +139,7 @@ std::vector<double> order_stat_probs(int M, int n) {
     for (int m = 0; m < M; ++m) p[m] += double(n - 2) * acc[m];
   }
   for (int m = 0; m < M; ++m) p[m] /= double(n);
+  if (!symmetric) return p;
   std::vector<double> sym(M);
   for (int m = 0; m < M; ++m) sym[m] = (p[m] + p[M - 1 - m]) / 2.0;
   return sym;
@@ -133,11 +182,37 @@ bool integer_table(const std::vector<double>& q, uint32_t* f) {
   return tot == 256;
 }
 
-bool build_side(int levels, int n, double alpha, int container_bytes, kvq::SideTables& s) {
+// Level values as stored (fp16): v_m = m, or the caller's values rounded to
+// fp16, which must rise strictly from 0 to levels - 1.
+bool level_values(int levels, const float* values, kvq::SideTables& s) {
+  s.affine = 1;
+  for (int m = 0; m < levels; ++m) {
+    const uint16_t h = f32_to_f16(values ? values[m] : float(m));
+    s.fp16_bits[m] = h;
+    s.fp16_hi[m] = h >> 8;
+    s.fp16_lo[m] = h & 0xFFu;
+    s.level[m] = f16_to_f32(h);
+    if (!std::isfinite(s.level[m])) return false;
+    if (s.level[m] != float(m)) s.affine = 0;
+  }
+  if (s.level[0] != 0.f || s.level[levels - 1] != float(levels - 1)) return false;
+  for (int m = 1; m < levels; ++m)
+    if (!(s.level[m] > s.level[m - 1])) return false;
+  return true;
+}
+
+bool build_side(int levels, int n, double alpha, int container_bytes, const float* values,
+                kvq::SideTables& s) {
   std::memset(&s, 0, sizeof(s));
   s.levels = levels;
   s.container_bytes = container_bytes;
-  std::vector<double> p = order_stat_probs(levels, n);
+  if (!level_values(levels, values, s)) return false;
+  std::vector<double> mids(levels - 1);
+  bool symmetric = true;
+  for (int m = 0; m + 1 < levels; ++m) mids[m] = 0.5 * (double(s.level[m]) + double(s.level[m + 1]));
+  for (int m = 0; m < levels; ++m)
+    if (double(s.level[m]) + double(s.level[levels - 1 - m]) != double(levels - 1)) symmetric = false;
+  std::vector<double> p = order_stat_probs(levels, n, mids, symmetric);
   std::vector<double> q(levels);
   double tot = 0.0;
   for (int m = 0; m < levels; ++m) {
@@ -170,17 +245,6 @@ bool build_side(int levels, int n, double alpha, int container_bytes, kvq::SideT
   for (int m = 0; m < levels; ++m)
     for (uint32_t z = s.cum[m]; z < s.cum[m] + s.freq[m]; ++z)
       s.dec[z] = s.freq[m] | ((z - s.cum[m]) << 8) | (uint32_t(m) << 16);
-  for (int m = 0; m < levels; ++m) {
-    // fp16 bit pattern of the integer m: exponent 15 + floor(log2 m), 10-bit mantissa
-    uint32_t bits = 0;
-    if (m > 0) {
-      int e = 0;
-      while ((2 << e) <= m) ++e;
-      const uint32_t mant = (uint32_t(m) << (10 - e)) & 0x3FFu;
-      bits = (uint32_t(15 + e) << 10) | mant;
-    }
-    s.fp16_hi[m] = bits >> 8;
-  }
   uint32_t cheap = 0;
   for (int m = 1; m < levels; ++m)
     if (s.rate_fx[m] < s.rate_fx[cheap]) cheap = m;
@@ -194,6 +258,11 @@ bool build_side(int levels, int n, double alpha, int container_bytes, kvq::SideT
 extern "C" {
 
 kvq_status kvq_plan_create(const kvq_params* params, kvq_plan** out_plan) {
+  return kvq_plan_create_levels(params, nullptr, nullptr, out_plan);
+}
+
+kvq_status kvq_plan_create_levels(const kvq_params* params, const float* values_k,
+                                  const float* values_v, kvq_plan** out_plan) {
   if (!params || !out_plan) return KVQ_EINVAL;
   *out_plan = nullptr;
   const kvq_params& p = *params;
@@ -213,8 +282,8 @@ kvq_status kvq_plan_create(const kvq_params* params, kvq_plan** out_plan) {
   if (!plan) return KVQ_ENOMEM;
   plan->params = p;
   plan->n = int(n);
-  if (!build_side(p.levels_k, int(n), p.sharpen_alpha, p.container_bytes_k, plan->side[0]) ||
-      !build_side(p.levels_v, int(n), p.sharpen_alpha, p.container_bytes_v, plan->side[1])) {
+  if (!build_side(p.levels_k, int(n), p.sharpen_alpha, p.container_bytes_k, values_k, plan->side[0]) ||
+      !build_side(p.levels_v, int(n), p.sharpen_alpha, p.container_bytes_v, values_v, plan->side[1])) {
     delete plan;
     return KVQ_EINVAL;
   }
@@ -247,6 +316,13 @@ kvq_status kvq_plan_tables(const kvq_plan* plan, int side, uint16_t* freq, uint1
   return KVQ_OK;
 }
 
+kvq_status kvq_plan_levels(const kvq_plan* plan, int side, float* values) {
+  if (!plan || (side != 0 && side != 1) || !values) return KVQ_EINVAL;
+  const kvq::SideTables& t = plan->side[side];
+  for (int m = 0; m < kvq::kMaxLevels; ++m) values[m] = m < t.levels ? t.level[m] : 0.f;
+  return KVQ_OK;
+}
+
 kvq_status kvq_plan_lambda_grid(const kvq_plan* plan, float* grid512) {
   if (!plan || !grid512) return KVQ_EINVAL;
   std::memcpy(grid512, plan->lambda_grid, sizeof(plan->lambda_grid));
@@ -256,7 +332,9 @@ kvq_status kvq_plan_lambda_grid(const kvq_plan* plan, float* grid512) {
 kvq_status kvq_model_probs(int32_t levels, int32_t n, double alpha, double* probs) {
   if (!probs || levels < 2 || levels > kvq::kMaxLevels || n < 2 || n > 4096) return KVQ_EINVAL;
   if (!(alpha >= 1.0) || !(alpha <= 16.0)) return KVQ_EINVAL;
-  const std::vector<double> p = order_stat_probs(levels, n);
+  std::vector<double> mids(levels - 1);
+  for (int m = 0; m + 1 < levels; ++m) mids[m] = m + 0.5;
+  const std::vector<double> p = order_stat_probs(levels, n, mids, true);
   double tot = 0.0;
   for (int m = 0; m < levels; ++m) tot += std::pow(p[m], alpha);
   for (int m = 0; m < levels; ++m) probs[m] = std::pow(p[m], alpha) / tot;

@@ -38,6 +38,8 @@ _P = ctypes.c_void_p
 _I32, _I64, _U64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
 _SIGS = {
     "kvq_plan_create": (_I32, [ctypes.POINTER(kvq_params), ctypes.POINTER(_P)]),
+    "kvq_plan_create_levels": (_I32, [ctypes.POINTER(kvq_params), _P, _P, ctypes.POINTER(_P)]),
+    "kvq_plan_levels": (_I32, [_P, ctypes.c_int, _P]),
     "kvq_plan_destroy": (None, [_P]),
     "kvq_plan_tables": (_I32, [_P, ctypes.c_int, _P, _P, _P]),
     "kvq_plan_lambda_grid": (_I32, [_P, _P]),
@@ -105,12 +107,24 @@ class Plan:
     """Owns a kvq_plan (host-side tables of one cache format)."""
 
     def __init__(self, n_kv_heads, head_dim, levels_k=8, levels_v=6, container_bytes_k=331,
-                 container_bytes_v=231, mean_window=128, sharpen_alpha=1.4):
+                 container_bytes_v=231, mean_window=128, sharpen_alpha=1.4, values_k=None, values_v=None):
         self.params = kvq_params(n_kv_heads, head_dim, levels_k, levels_v, container_bytes_k,
                                  container_bytes_v, mean_window, sharpen_alpha)
         h = ctypes.c_void_p()
-        _check("kvq_plan_create", lib().kvq_plan_create(ctypes.byref(self.params), ctypes.byref(h)))
+        if values_k is None and values_v is None:
+            _check("kvq_plan_create", lib().kvq_plan_create(ctypes.byref(self.params), ctypes.byref(h)))
+        else:
+            arr = lambda vals: None if vals is None else (ctypes.c_float * len(vals))(*vals)
+            _check("kvq_plan_create_levels", lib().kvq_plan_create_levels(
+                ctypes.byref(self.params), arr(values_k), arr(values_v), ctypes.byref(h)))
         self.handle = h
+
+    def levels(self, side):
+        """Level values v_m as stored (floats) for side 0 (K) / 1 (V)."""
+        out = (ctypes.c_float * 16)()
+        _check("kvq_plan_levels", lib().kvq_plan_levels(self.handle, side, out))
+        M = self.params.levels_k if side == 0 else self.params.levels_v
+        return list(out)[:M]
 
     def __del__(self):
         h = getattr(self, "handle", None)

@@ -30,6 +30,15 @@ def _encode_chunk(args):
     return {key: r[key] for key in keep}
 
 
+def _param_dict(p):
+    """OracleParams fields a worker needs to rebuild the same parameters."""
+    return dict(n_kv_heads=p.n_kv_heads, head_dim=p.head_dim, levels_k=p.levels_k,
+                levels_v=p.levels_v, container_bytes_k=p.container_bytes_k,
+                container_bytes_v=p.container_bytes_v, mean_window=p.mean_window, alpha=p.alpha,
+                values_k=None if p.values_k is None else tuple(float(x) for x in p.values_k),
+                values_v=None if p.values_v is None else tuple(float(x) for x in p.values_v))
+
+
 def n_workers():
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -40,9 +49,7 @@ def encode_cache_parallel(k, v, p, procs=None, chunk_windows=1):
     v = np.asarray(v, np.float32)
     T = k.shape[0]
     step = p.mean_window * chunk_windows
-    pdict = dict(n_kv_heads=p.n_kv_heads, head_dim=p.head_dim, levels_k=p.levels_k,
-                 levels_v=p.levels_v, container_bytes_k=p.container_bytes_k,
-                 container_bytes_v=p.container_bytes_v, mean_window=p.mean_window, alpha=p.alpha)
+    pdict = _param_dict(p)
     jobs = [(k[t:t + step], v[t:t + step], pdict) for t in range(0, T, step)]
     procs = procs or n_workers()
     if procs == 1 or len(jobs) == 1:
@@ -71,8 +78,10 @@ def _decode_attention_job(job):
     k_sym, _, _ = O.rans_decode(r["k_cont"], fk, ck, p.n)
     v_sym, _, _ = O.rans_decode(r["v_cont"], fv, cv, p.n)
     mu_tok = np.repeat(r["mu_hat"], p.mean_window, axis=0)
+    kv = None if p.values_k is None else p.vals("k")
+    vv = None if p.values_v is None else p.vals("v")
     return O.attention_factored_f64(q, k_sym, r["k_so"], mu_tok, v_sym, r["v_so"],
-                                    p.n_kv_heads, p.head_dim)
+                                    p.n_kv_heads, p.head_dim, k_vals=kv, v_vals=vv)
 
 
 def time_decode_attention(refs, qs, p, procs, repeats=1, target_s=None):
@@ -81,9 +90,7 @@ def time_decode_attention(refs, qs, p, procs, repeats=1, target_s=None):
     list is repeated until one timed pass is expected to take about that long.
     Returns (seconds, tasks timed, outputs of the first len(refs) tasks)."""
     import time
-    pdict = dict(n_kv_heads=p.n_kv_heads, head_dim=p.head_dim, levels_k=p.levels_k,
-                 levels_v=p.levels_v, container_bytes_k=p.container_bytes_k,
-                 container_bytes_v=p.container_bytes_v, mean_window=p.mean_window, alpha=p.alpha)
+    pdict = _param_dict(p)
     slim = [{k: r[k] for k in ("k_cont", "v_cont", "k_so", "v_so", "mu_hat")} for r in refs]
     base = [(slim[i], qs[i], pdict) for i in range(len(refs))]
     with mp.get_context("spawn").Pool(procs, initializer=_init_worker, initargs=(pdict,)) as pool:

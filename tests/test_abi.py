@@ -153,3 +153,29 @@ def test_fixed_width_sizes_and_errors():
     fw = kvq.Plan(8, 128, 16, 3, 512, 256)                 # 16 key levels: no 4-entry level lookup
     assert L.kvq_decode_attention_fixed_width(fw.handle, a16, 32, a16, a16, a16, a16, a16, a16, 1, 128, 0.0,
                                               a16, None, a16, 1 << 30, st) == -3
+
+
+@pytest.mark.parametrize("values_k,values_v", [
+    ((0.0, 0.75, 1.875, 3.0, 4.0, 5.125, 6.25, 7.0), (0.0, 0.875, 2.125, 2.875, 4.125, 5.0)),
+    ((0.0, 0.3, 1.1, 3.0), None),
+    (None, (0.0, 0.5, 1.75, 3.25, 4.0)),
+])
+def test_planner_tables_with_levels_match_oracle(values_k, values_v):
+    _lib()
+    mk = len(values_k) if values_k else 8
+    mv = len(values_v) if values_v else 6
+    plan = kvq.Plan(8, 128, mk, mv, 331, 231, 128, 1.4, values_k=values_k, values_v=values_v)
+    p = O.OracleParams(8, 128, mk, mv, 331, 231, 128, 1.4, values_k=values_k, values_v=values_v)
+    for side, key in ((0, "k"), (1, "v")):
+        f, c, r = p.table(key)
+        pf, pc, pr = plan.tables(side)
+        assert pf == f.tolist() and pc == c.tolist() and pr == r.tolist()
+        assert np.array_equal(np.array(plan.levels(side), np.float32), p.vals(key))
+
+
+def test_planner_rejects_bad_levels():
+    _lib()
+    for vk in ((0.5, 1.0, 2.0, 3.0), (0.0, 1.0, 1.0, 3.0), (0.0, 1.0, 2.0, 2.5)):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.Plan(8, 128, 4, 6, 331, 231, values_k=vk)
+        assert e.value.status == -1

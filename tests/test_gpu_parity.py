@@ -54,8 +54,11 @@ def gpu_attention(kvq, plan, q, c, Hq):
 
 def oracle_attention(q, r, p):
     mu_tok = np.repeat(r["mu_hat"], p.mean_window, axis=0)
+    kv = None if p.values_k is None else p.vals("k")
+    vv = None if p.values_v is None else p.vals("v")
     return O.attention_factored_f64(q.astype(np.float64), r["k_sym"], r["k_so"], mu_tok,
-                                    r["v_sym"], r["v_so"], p.n_kv_heads, p.head_dim)
+                                    r["v_sym"], r["v_so"], p.n_kv_heads, p.head_dim,
+                                    k_vals=kv, v_vals=vv)
 
 
 def check_attention(out, out32, ref):
@@ -83,15 +86,16 @@ def compare_cache(c, stats, refs, p, S):
     assert stats.cpu().numpy().astype(np.uint64).tolist() == tot.tolist()
 
 
-def run_case(name, budget_idx, seqs, tokens, w=None, levels=(8, 6)):
+def run_case(name, budget_idx, seqs, tokens, w=None, levels=(8, 6), values=(None, None)):
     kvq = _kvq()
     w = w or synth.WORKLOADS[name]
     ck, cv = w.containers[budget_idx]
     mk, mv = levels
     say(f"case {w.name} budget={w.budgets[budget_idx]} C=({ck},{cv}) M=({mk},{mv}) "
         f"heads={w.n_q_heads}/{w.n_kv_heads} seqs={seqs} tokens={tokens}")
-    plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4)
-    p = O.OracleParams(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4)
+    plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4, values_k=values[0], values_v=values[1])
+    p = O.OracleParams(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4, values_k=values[0],
+                       values_v=values[1])
     k, v = synth.cache_inputs(w, "cuda", seqs, tokens)
     q = synth.queries(w, "cuda", seqs)
     c, stats = gpu_encode(kvq, plan, k, v)
@@ -156,3 +160,15 @@ def test_encode_is_deterministic():
     for key in a:
         assert torch.equal(a[key], b[key])
     assert torch.equal(sa, sb)
+
+
+@pytest.mark.parametrize("levels,values,cont", [
+    ((8, 6), ((0.0, 0.75, 1.875, 3.0, 4.0, 5.125, 6.25, 7.0), (0.0, 0.875, 2.125, 2.875, 4.125, 5.0)),
+     (331, 231)),
+    ((12, 4), ((0.0, 0.5, 1.25, 2.5, 3.75, 5.0, 6.0, 7.25, 8.5, 9.75, 10.5, 11.0), (0.0, 0.625, 2.0, 3.0)),
+     (380, 190)),
+])
+def test_non_affine_levels(levels, values, cont):
+    # [D-Quant] Appendix A: table entries carry arbitrary reconstruction levels
+    w = synth.Workload("levels", 32, 8, 128, 2, 1, 640, 41, "keymeans", (cont,), (0.0,))
+    run_case(None, 0, [0, 1], None, w=w, levels=levels, values=values)
