@@ -603,6 +603,25 @@ __device__ inline uint32_t dec5_step(uint32_t& x, uint32_t win, uint32_t& sel, c
   return e;
 }
 
+// 4x4x4 MFMA whose A operand is broadcast from block `abid` to all 16 blocks.
+// The builtin needs the block as a literal; callers pass a value that is a
+// constant after unrolling, so the switch folds to one instruction.
+__device__ __attribute__((always_inline)) inline float4_t mfma_bcast_a(half4_t a, half4_t b, float4_t c,
+                                                                       int abid) {
+#define KVQ_MFMA_BCAST_CASE(i) \
+  case i:                      \
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, i, 0);
+  switch (abid) {
+    KVQ_MFMA_BCAST_CASE(0) KVQ_MFMA_BCAST_CASE(1) KVQ_MFMA_BCAST_CASE(2) KVQ_MFMA_BCAST_CASE(3)
+    KVQ_MFMA_BCAST_CASE(4) KVQ_MFMA_BCAST_CASE(5) KVQ_MFMA_BCAST_CASE(6) KVQ_MFMA_BCAST_CASE(7)
+    KVQ_MFMA_BCAST_CASE(8) KVQ_MFMA_BCAST_CASE(9) KVQ_MFMA_BCAST_CASE(10) KVQ_MFMA_BCAST_CASE(11)
+    KVQ_MFMA_BCAST_CASE(12) KVQ_MFMA_BCAST_CASE(13) KVQ_MFMA_BCAST_CASE(14)
+    default:
+      return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, 15, 0);
+  }
+#undef KVQ_MFMA_BCAST_CASE
+}
+
 // PV over the 64 tokens of a tile for 64 channels: the int8 level indices of
 // the [channel][token] chunk become fp16 through v_perm lookups (high bytes;
 // with LO also the low bytes of non-integer levels) and are contracted on
@@ -686,6 +705,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   const uint32_t lutLo2 = a.lbv[0] | (a.lbv[1] << 8) | (a.lbv[2] << 16) | (a.lbv[3] << 24);
   const uint32_t lutHi2 = a.lbv[4] | (a.lbv[5] << 8) | (a.lbv[6] << 16) | (a.lbv[7] << 24);
 
+  // Output accumulators, rotated once per head step so that the loop over
+  // heads needs no register indexing: at the start of step g, O[j] holds KV
+  // head (g - 1 + j) mod HKV, so V's head is O[0] and K's head is O[KJ].
+  constexpr int KJ = 1 % HKV;
   float4_t O[HKV][2][NGM];
 #pragma unroll
   for (int g = 0; g < HKV; ++g)
@@ -702,6 +725,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   const float* qsum = a.qsum + s * HQ;
   const float* qmu = a.qmu + s * HQ * a.nW;
   const int qn = lane & 3;
+  // The query operand of channel quad c = 16 ch + 8 t + j (ch, t in {0, 1},
+  // j < 8) is held by the lanes of MFMA block 8 ch + j, in register t: each
+  // QK^T MFMA broadcasts that block's A operand to all 16 blocks (CBSZ = 4,
+  // ABID = 8 ch + j), so one head's query takes two registers per lane and
+  // is loaded once per head, a head ahead, not once per channel quad.
+  // (With two MFMA groups of query heads the prefetch would not fit the
+  // register file; the head's query is then loaded at the head's start.)
+  const int qc0 = 16 * ((lane >> 2) >> 3) + ((lane >> 2) & 7);
+  constexpr bool kQPrefetch = NGM == 1;
+  uint4 qnx[NGM][2];
+#pragma unroll
+  for (int m = 0; m < NGM; ++m)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) qnx[m][t] = kQPrefetch ? qop[(m * 32 + qc0 + 8 * t) * 4 + qn] : uint4{};
   const uint16_t* const wv = wts;                 // weights of the head whose V is decoded
   const uint16_t* const wv_lo = wts + NW * 64;
 
@@ -718,7 +755,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   for (int64_t i = 0; i <= NT; ++i) {
     const bool kreal = i < NT;
     const int64_t tK = tb + 64 * (kreal ? i : NT - 1);        // K tile (clamped dummy)
-#pragma unroll
+#pragma unroll 1
     for (int g = 0; g < HKV; ++g) {
       if (!kreal && g > 0) break;
       // ---- stream starts
@@ -749,16 +786,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
       float4_t D[NGM];
 #pragma unroll
       for (int m = 0; m < NGM; ++m) D[m] = float4_t{0.f, 0.f, 0.f, 0.f};
-      const uint4* qg = qop + g * (NGM * 32 * 4) + qn;
-      uint4 qa[NGM];
+      uint4 qh[NGM][2];
+      {
+        const int gn = kQPrefetch ? (g + 1 < HKV ? g + 1 : 0) : g;    // the head whose query is loaded
+        const uint4* qg = qop + gn * (NGM * 32 * 4) + qn;
 #pragma unroll
-      for (int m = 0; m < NGM; ++m) qa[m] = qg[(m * 32) * 4];
+        for (int m = 0; m < NGM; ++m)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (kQPrefetch) {
+              qh[m][t] = qnx[m][t];
+              qnx[m][t] = qg[(m * 32 + qc0 + 8 * t) * 4];
+            } else {
+              qh[m][t] = qg[(m * 32 + qc0 + 8 * t) * 4];
+            }
+          }
+      }
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll 1
-        for (int b4 = 0; b4 < 4; ++b4) {
-          const int blk = ch * 4 + b4;
-          if (b4 & 1) {
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int bh = 0; bh < 2; ++bh) {
+          // two blocks per trip, one per refill slot: each slot's chunk stays
+          // in the same registers across the loop's back edge
+          const int b4 = 2 * b2 + bh;
+          if (bh == 1) {
             ring5_block<1>(rk, lds, rsK);
             ring5_block<1>(rv, lds, rsV);
           } else {
@@ -767,11 +820,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
           }
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
-            const int c = blk * 4 + cc;
-            const int cn = c + 1 < 32 ? c + 1 : 31;
-            uint4 qb[NGM];
-#pragma unroll
-            for (int m = 0; m < NGM; ++m) qb[m] = qg[(m * 32 + cn) * 4];
             uint32_t e[4];
             const uint32_t winK = ring5_window(rk, lds), winV = ring5_window(rv, lds);
             uint32_t selk = kSel0, selv = kSel0;
@@ -787,18 +835,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
                                        __builtin_amdgcn_perm(e[3], e[2], 0x07060302u));
 #pragma unroll
             for (int m = 0; m < NGM; ++m) {
-              D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(qa[m].x, qa[m].y), B, D[m], 0, 0, 0);
-              D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(qa[m].z, qa[m].w), B, D[m], 0, 0, 0);
-              qa[m] = qb[m];
+              D[m] = mfma_bcast_a(as_half4(qh[m][0].x, qh[m][0].y), B, D[m], 8 * ch + 4 * bh + cc);
+              D[m] = mfma_bcast_a(as_half4(qh[m][0].z, qh[m][0].w), B, D[m], 8 * ch + 4 * bh + cc);
+            }
+          }
+          if (bh == 1) {
+            // the trip's second half is done: the other register's quads come next
+#pragma unroll
+            for (int m = 0; m < NGM; ++m) {
+              const uint4 t = qh[m][0];
+              qh[m][0] = qh[m][1];
+              qh[m][1] = t;
             }
           }
         }
         // PV of V's head for the 64 channels of this half
         wave_lds_fence();
         if (a.v_lo_nonzero)
-          pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[vg][ch]);
+          pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[0][ch]);
         else
-          pv_half<NGM, false>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, 0u, 0u, O[vg][ch]);
+          pv_half<NGM, false>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, 0u, 0u, O[0][ch]);
         wave_lds_fence();
       }
       // ---- K head g done: logits -> online softmax -> weights for the next iteration
@@ -822,7 +878,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
             runL[h] = Lo * al + ls;
             runZ[h] = Zo * al + zs;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) O[g][c][m][ii] *= al;
+            for (int c = 0; c < 2; ++c) O[KJ][c][m][ii] *= al;
             const float wt = p * svK;
             const __half hh = __float2half_rn(wt);
             whi = wt;
@@ -833,8 +889,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
         }
         wave_lds_fence();
       }
+      // rotate: the next step's V head (this step's K head) becomes O[0]
+      if (HKV > 1) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int m = 0; m < NGM; ++m) {
+            const float4_t t = O[0][c][m];
+#pragma unroll
+            for (int j = 0; j + 1 < HKV; ++j) O[j][c][m] = O[j + 1][c][m];
+            O[HKV - 1][c][m] = t;
+          }
+      }
     }
   }
+  // The last step (i = NT, g = 0) rotated too, so O[j] now holds KV head j.
 
   float* P = a.part + (s * a.part_splits + split) * int64_t(HQ) * (kD + 4);
 #pragma unroll

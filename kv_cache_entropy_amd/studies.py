@@ -63,11 +63,36 @@ class Sample:
         return (a @ V).reshape(self.S, w.n_q_heads, w.head_dim)
 
 
-def run_config(sm, mk, mv, ck, cv, attention=True):
-    """Encodes the sample with one format; returns errors and symbol statistics."""
+def lloyd_max_levels(M, n, streams=4000, iters=60, seed=0):
+    """Non-affine reconstruction levels in grid units for min-max normalised
+    N(0,1) streams of length n: Lloyd-Max iteration (start at the quantiles,
+    then alternate nearest-level assignment and centroid update), as
+    KVQuant-style non-uniform quantisers do.  Every stream puts its minimum at
+    0 and its maximum at M - 1, so those two levels stay pinned and only the
+    interior ones move.  Returns a tuple of M floats."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((streams, n))
+    u = (x - x.min(1, keepdims=True)) / (x.max(1, keepdims=True) - x.min(1, keepdims=True)) * (M - 1)
+    u = np.sort(u.ravel())
+    lv = np.quantile(u, (np.arange(M) + 0.5) / M)
+    lv[0], lv[-1] = 0.0, M - 1.0
+    for _ in range(iters):
+        cut = np.searchsorted(u, (lv[1:] + lv[:-1]) / 2)
+        for m in range(1, M - 1):
+            seg = u[cut[m - 1]:cut[m]]
+            if seg.size:
+                lv[m] = seg.mean()
+    return tuple(float(v) for v in lv)
+
+
+def run_config(sm, mk, mv, ck, cv, attention=True, values=(None, None)):
+    """Encodes the sample with one format; returns errors and symbol statistics.
+    values: optional non-affine levels (grid units) for K and V."""
     w = sm.w
     try:
-        plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4)
+        plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4,
+                        values_k=values[0], values_v=values[1])
     except kvq.KvqError as e:
         if e.status == -2:            # KVQ_EINFEASIBLE: the alphabet does not fit
             return None
@@ -87,7 +112,8 @@ def run_config(sm, mk, mv, ck, cv, attention=True):
         sym = torch.empty(sm.S, sm.T, w.n, dtype=torch.uint8, device="cuda")
         kvq.kvq_decode_symbols(plan, side, c[key], sym)
         so = c[so_key].view(torch.float16).double()
-        rec = so[..., 0:1] * sym.double() + so[..., 1:2]
+        lv = torch.tensor(plan.levels(side), dtype=torch.float64, device="cuda")
+        rec = so[..., 0:1] * lv[sym.long()] + so[..., 1:2]
         if side == 0:
             rec = rec + mu_tok
         name = "k" if side == 0 else "v"
@@ -102,7 +128,8 @@ def run_config(sm, mk, mv, ck, cv, attention=True):
         H = float(-(ph[nz] * torch.log2(ph[nz])).sum())
         out[f"entropy_{name}"] = H
         out[f"coding_gain_{name}"] = math.log2(M) - H
-        out[f"model_gap_{name}"] = float(-(ph[nz] * torch.log2(model[nz])).sum()) - H
+        out[f"model_gap_{name}"] = (float(-(ph[nz] * torch.log2(model[nz])).sum()) - H
+                                    if values[side] is None else None)
         out[f"table_gap_{name}"] = float(-(ph[nz] * torch.log2(table[nz])).sum()) - H
         out[f"hist_{name}"] = [round(float(x), 5) for x in ph]
         if side == 0:
@@ -257,6 +284,23 @@ def main(argv=None):
           f"{fw['nmse_k']:.4%} | {fw['nmse_v']:.4%} | {fw['attn_rel_err']:.4%} |")
     print("\n(The page charges the fixed-width format the ideal log2 6 + log2 3 bits, i.e. the same "
           "2.26 bits/value; stored at power-of-two widths it takes the bytes above.)")
+    # non-affine levels: Lloyd-Max levels of min-max normalised Gaussian streams
+    lk, lvv = lloyd_max_levels(8, sm.w.n), lloyd_max_levels(6, sm.w.n)
+    res["non_affine"] = {"levels_k": lk, "levels_v": lvv, "rows": []}
+    print("\n## Non-affine reconstruction levels (Lloyd-Max levels for min-max normalised Gaussian streams)\n")
+    print(f"* K levels (grid units) {[round(x, 4) for x in lk]}")
+    print(f"* V levels (grid units) {[round(x, 4) for x in lvv]}\n")
+    print("| levels | C_K/C_V | K NMSE | V NMSE | attention rel. error | K changed | V changed | H_K | H_V |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|---:|")
+    for ck, cv in ((400, 400), (331, 231), (292, 203)):
+        for name, vals in (("affine", (None, None)), ("Lloyd-Max", (lk, lvv))):
+            r = run_config(sm, 8, 6, ck, cv, values=vals)
+            res["non_affine"]["rows"].append(dict(kind=name, ck=ck, cv=cv, **(r or {})))
+            if r is None:
+                print(f"| {name} | {ck}/{cv} | — | — | — | — | — | — | — |")
+                continue
+            print(f"| {name} | {ck}/{cv} | {r['nmse_k']:.4%} | {r['nmse_v']:.4%} | {r['attn_rel_err']:.4%} | "
+                  f"{r['changed_k']:.3%} | {r['changed_v']:.3%} | {r['entropy_k']:.4f} | {r['entropy_v']:.4f} |")
     if args.json:
         with open(args.json, "w") as fh:
             json.dump(res, fh, indent=1)
