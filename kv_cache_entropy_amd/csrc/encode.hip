@@ -83,9 +83,111 @@ __global__ __launch_bounds__(1024) void key_mean_kernel(KeyMeanArgs a) {
 // Drift (Algorithm 1) for the stream held NPL values per lane by one wave.
 // Returns true if the encoder fell back to the cheapest symbol everywhere.
 // If near != nullptr, the nearest-level (lambda -> 0) assignment is returned.
-template <int NPL>
+//
+// With at most MC levels the distortions D_im = (x_i - rec_m)^2 are computed
+// once and kept in registers: they do not depend on lambda, so each bisection
+// step only adds lambda r_m and takes the argmin.  The values are the same
+// roundings as recomputing them, so the result is identical.
+template <int NPL, int MC>
 __device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& sh,
                       int levels, uint8_t (&m)[NPL], uint8_t (*near)[NPL]) {
+  // distortions, their range over all (i, level), and the nearest levels
+  float dmax = 0.f, dmin = __builtin_inff();
+  float Dc[MC][NPL];
+  float bestD[NPL];
+  uint32_t bl[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) { bestD[i] = __builtin_inff(); bl[i] = 0; }
+#pragma unroll
+  for (int l = 0; l < MC; ++l) {
+    if (l < levels) {
+      const float rec = __fadd_rn(o, __fmul_rn(s, sh.level[l]));
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const float dl = __fsub_rn(x[i], rec);
+        const float D = __fmul_rn(dl, dl);
+        Dc[l][i] = D;
+        dmax = fmaxf(dmax, D);
+        dmin = fminf(dmin, D);
+        const bool lt = D < bestD[i];
+        bestD[i] = lt ? D : bestD[i];
+        bl[i] = lt ? uint32_t(l) : bl[i];
+      }
+    }
+  }
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) (*near)[i] = uint8_t(bl[i]);
+  }
+  dmax = wave_max(dmax);
+  dmin = wave_min(dmin);
+  const float y = __fmul_rn(__fsub_rn(dmax, dmin), 8.0f);
+  const uint8_t cheap = uint8_t(sh.cheapest);
+  if (!(y > 0.f)) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) m[i] = cheap;
+    return false;
+  }
+  int e;
+  const float fr = frexpf(y, &e);
+  const int hi0 = (fr == 0.5f) ? e - 1 : e;
+  int lo = 512 * (hi0 - 40), hi = 512 * hi0;
+  bool moved = false;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) m[i] = cheap;
+  uint32_t cur[NPL];
+  for (int step = 0; step <= 12; ++step) {
+    int u;
+    if (step < 12) {
+      u = (lo + hi) >> 1;              // lo + hi is always even: exact
+    } else {
+      if (moved) break;
+      u = hi;                          // never feasible inside: try 2^hi
+    }
+    const float lam = ldexpf(sh.lambda[u & 511], u >> 9);
+    float best[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) { best[i] = __builtin_inff(); cur[i] = 0; }
+#pragma unroll
+    for (int l = 0; l < MC; ++l) {
+      if (l < levels) {
+        const float lr = __fmul_rn(lam, sh.rate_f[l]);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          const float obj = __fadd_rn(Dc[l][i], lr);
+          const bool lt = obj < best[i];
+          best[i] = lt ? obj : best[i];
+          cur[i] = lt ? uint32_t(l) : cur[i];
+        }
+      }
+    }
+    uint32_t R = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) R += sh.rate_fx[cur[i]];
+    R = wave_sum_u32(R);
+    const bool ok = uint64_t(R) <= sh.budget_fx;
+    if (step < 12) {
+      if (ok) {
+        hi = u;
+        moved = true;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) m[i] = uint8_t(cur[i]);
+      } else {
+        lo = u;
+      }
+    } else {
+      if (!ok) return true;            // fallback: cheapest level everywhere
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) m[i] = uint8_t(cur[i]);
+    }
+  }
+  return false;
+}
+
+// The same without the cache, for alphabets above MC levels.
+template <int NPL>
+__device__ bool drift_large(const float (&x)[NPL], float s, float o, const EncShared& sh,
+                            int levels, uint8_t (&m)[NPL], uint8_t (*near)[NPL]) {
   // range of the distortion over all (i, level) and the nearest levels
   float dmax = 0.f, dmin = __builtin_inff();
   float bestD[NPL];
@@ -289,6 +391,10 @@ __device__ bool rans_encode_lane(const uint8_t* sym, int n, uint8_t* img, int C,
 // Algorithm 1 on SPW/4 streams in turn (values stay in registers); then SPW
 // lanes rANS-code the streams from LDS and the workgroup copies the SPW
 // contiguous containers out with dword stores.
+// Alphabets up to this size keep the drift distortions in registers (for
+// streams of up to 16 values per lane: 128 registers).
+constexpr int kDriftCache = 8;
+
 template <int NPL, int FWB>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   constexpr bool FW = FWB != 0;
@@ -347,10 +453,17 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
       nearest<NPL>(x, __half2float(s16), __half2float(o16), M, sh.level, m);
       if constexpr (FW) fw_pack_lane<NPL, FWB>(m, reinterpret_cast<uint32_t*>(img + size_t(sl) * C), lane);
     } else {
-      fb1 += drift<NPL>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
-      refit<NPL>(x, m, s, o, n, sh.level, s16, o16);
       uint8_t near[NPL];
-      fb2 += drift<NPL>(x, __half2float(s16), __half2float(o16), sh, M, m, &near) ? 1u : 0u;
+      if (NPL * kDriftCache <= 128 && M <= kDriftCache) {
+        constexpr int MC = NPL * kDriftCache <= 128 ? kDriftCache : 1;
+        fb1 += drift<NPL, MC>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
+        refit<NPL>(x, m, s, o, n, sh.level, s16, o16);
+        fb2 += drift<NPL, MC>(x, __half2float(s16), __half2float(o16), sh, M, m, &near) ? 1u : 0u;
+      } else {
+        fb1 += drift_large<NPL>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
+        refit<NPL>(x, m, s, o, n, sh.level, s16, o16);
+        fb2 += drift_large<NPL>(x, __half2float(s16), __half2float(o16), sh, M, m, &near) ? 1u : 0u;
+      }
       uint32_t ch = 0;
 #pragma unroll
       for (int i = 0; i < NPL; ++i) ch += (m[i] != near[i]) ? 1u : 0u;
