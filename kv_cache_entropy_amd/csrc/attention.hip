@@ -219,12 +219,29 @@ __global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
     a.qsum[s * a.Hq + h] = qs;
     a.qscale[s * a.Hq + h] = ldexpf(1.0f, -e);
   }
-  for (int64_t w = 0; w < a.nW; ++w) {
+  // sum_j q_rot_j mu_w,j: one window per lane at a time, so that the windows'
+  // loads are independent (a long context has thousands of windows per head);
+  // each lane reads its window's 128 int8 means as 16-byte vectors (rows are
+  // 16-byte aligned: the base is, and n is a multiple of 128).
+  __shared__ float qsh[kD];
+  qsh[2 * lane] = q[0];
+  qsh[2 * lane + 1] = q[1];
+  __syncthreads();
+  for (int64_t w = lane; w < a.nW; w += 64) {
     const float sc = h2f(a.mean_scale[s * a.nW_cap + w]);
-    const int8_t* mq = a.mean_q + (s * a.nW_cap + w) * a.n + int64_t(g) * kD + lane * 2;
-    float acc = q[0] * __fmul_rn(float(mq[0]), sc) + q[1] * __fmul_rn(float(mq[1]), sc);
-    acc = wave_sum_f(acc);
-    if (lane == 0) a.qmu[(s * a.Hq + h) * a.nW + w] = acc;
+    const uint4* mq = reinterpret_cast<const uint4*>(a.mean_q + (s * a.nW_cap + w) * a.n + int64_t(g) * kD);
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v4 = mq[c];
+      const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float mu = __fmul_rn(float(int8_t(wd[k / 4] >> (8 * (k % 4)))), sc);
+        acc = __fadd_rn(acc, __fmul_rn(qsh[16 * c + k], mu));
+      }
+    }
+    a.qmu[(s * a.Hq + h) * a.nW + w] = acc;
   }
 }
 

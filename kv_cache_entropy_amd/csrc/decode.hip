@@ -52,26 +52,75 @@ __global__ __launch_bounds__(256) void decode_symbols_kernel(DecSymArgs a) {
 }
 
 // ----------------------------------------------------------------- combine
+// One workgroup per (query head, sequence).  Its waves share the splits: each
+// merges a contiguous range (the max and per-split weights spread over the
+// lanes, the weighted sum of partial outputs over 64 splits at a time with
+// independent loads), then wave 0 merges the waves' results through LDS, undoes
+// the rotation and stores.  A single long sequence has thousands of splits.
+constexpr int kCombineMaxWaves = 16;
+
 template <int NPL>
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int h = blockIdx.x;
   const int64_t s = blockIdx.y;
   const int stride = a.d + 4;
   const float* P = a.part + (s * a.nsplit) * int64_t(a.Hq) * stride + int64_t(h) * stride;
   const int64_t sp = int64_t(a.Hq) * stride;
+  const int per = (a.nsplit + nwv - 1) / nwv;
+  const int kb = wv * per;
+  const int ke = kb + per < a.nsplit ? kb + per : a.nsplit;
   float Mx = -__builtin_inff();
-  for (int k = 0; k < a.nsplit; ++k) Mx = fmaxf(Mx, P[k * sp + a.d]);
+  for (int k = kb + lane; k < ke; k += 64) Mx = fmaxf(Mx, P[k * sp + a.d]);
+  Mx = wave_max(Mx);
   float L = 0.f, Z = 0.f;
   float acc[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) acc[i] = 0.f;
-  for (int k = 0; k < a.nsplit; ++k) {
-    const float sc = __expf(P[k * sp + a.d] - Mx);
-    L += sc * P[k * sp + a.d + 1];
-    Z += sc * P[k * sp + a.d + 2];
+  if (Mx > -__builtin_inff()) {
+    for (int k0 = kb; k0 < ke; k0 += 64) {
+      const int k = k0 + lane;
+      float sck = 0.f, lk = 0.f, zk = 0.f;
+      if (k < ke) {
+        sck = __expf(P[k * sp + a.d] - Mx);
+        lk = sck * P[k * sp + a.d + 1];
+        zk = sck * P[k * sp + a.d + 2];
+      }
+      L += wave_sum_f32(lk);
+      Z += wave_sum_f32(zk);
+      const int kn = ke - k0 < 64 ? ke - k0 : 64;
+#pragma unroll 8
+      for (int j = 0; j < kn; ++j) {
+        const float sc = __shfl(sck, j, 64);
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) acc[i] += sc * P[k * sp + lane * NPL + i];
+        for (int i = 0; i < NPL; ++i) acc[i] += sc * P[int64_t(k0 + j) * sp + lane * NPL + i];
+      }
+    }
+  }
+  if (nwv > 1) {
+    __shared__ float red[kCombineMaxWaves][64 * NPL + 4];
+    if (lane == 0) {
+      red[wv][64 * NPL] = Mx;
+      red[wv][64 * NPL + 1] = L;
+      red[wv][64 * NPL + 2] = Z;
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) red[wv][lane * NPL + i] = acc[i];
+    __syncthreads();
+    if (wv != 0) return;
+    float M = -__builtin_inff();
+    for (int w = 0; w < nwv; ++w) M = fmaxf(M, red[w][64 * NPL]);
+    L = 0.f;
+    Z = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) acc[i] = 0.f;
+    for (int w = 0; w < nwv; ++w) {
+      const float sc = __expf(red[w][64 * NPL] - M);     // 0 for a wave without splits
+      L += sc * red[w][64 * NPL + 1];
+      Z += sc * red[w][64 * NPL + 2];
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) acc[i] += sc * red[w][lane * NPL + i];
+    }
   }
   const float inv = 1.0f / L;
 #pragma unroll
@@ -212,10 +261,14 @@ hipError_t launch_decode_symbols(const DecSymArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream) {
   const dim3 grid(a.Hq, unsigned(S));
+  // about 128 splits per wave, up to 16 waves per (query head, sequence)
+  int waves = (a.nsplit + 127) / 128;
+  waves = waves < 1 ? 1 : (waves > kCombineMaxWaves ? kCombineMaxWaves : waves);
+  const dim3 block(64 * waves);
   switch (a.d) {
-    case 64: hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(64), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(64), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(64), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
