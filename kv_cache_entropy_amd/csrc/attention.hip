@@ -149,12 +149,22 @@ __device__ inline float swap_rows_sum(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(r), __float_as_uint(r), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);             // own + partner half
 }
-__device__ inline float swap_rows_max(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float r = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(r), __float_as_uint(r), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+// The max runs on order-preserving integer keys of the (finite) floats: an
+// integer max takes its DPP operand directly, where fmaxf would first quiet
+// both operands.  Lanes without a DPP source would keep INT_MIN, the max's
+// identity (every pattern used here is a full permutation).
+template <int CTRL>
+__device__ inline int dpp_max_i(int v) {
+  const int o = __builtin_amdgcn_update_dpp(int(0x80000000), v, CTRL, 0xF, 0xF, false);
+  return v > o ? v : o;
 }
+__device__ inline int swap_rows_max_i(int v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(uint32_t(v), uint32_t(v), false, false);
+  const int r = int(a[0]) > int(a[1]) ? int(a[0]) : int(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(uint32_t(r), uint32_t(r), false, false);
+  return int(b[0]) > int(b[1]) ? int(b[0]) : int(b[1]);
+}
+__device__ inline int float_key(int b) { return b ^ ((b >> 31) & 0x7FFFFFFF); }
 __device__ inline float wave_sum_dpp(float v) {
   v += dpp_f<0xB1>(v);      // quad_perm [1,0,3,2]
   v += dpp_f<0x4E>(v);      // quad_perm [2,3,0,1]
@@ -163,11 +173,12 @@ __device__ inline float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(swap_rows_sum(v))));
 }
 __device__ inline float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x124>(v));
-  v = fmaxf(v, dpp_f<0x128>(v));
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(swap_rows_max(v))));
+  int k = float_key(__float_as_int(v));
+  k = dpp_max_i<0xB1>(k);
+  k = dpp_max_i<0x4E>(k);
+  k = dpp_max_i<0x124>(k);
+  k = dpp_max_i<0x128>(k);
+  return __int_as_float(float_key(__builtin_amdgcn_readfirstlane(swap_rows_max_i(k))));
 }
 
 // ------------------------------------------------------------------ prologue
