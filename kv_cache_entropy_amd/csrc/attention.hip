@@ -556,7 +556,9 @@ struct Ring5 {
 };
 
 __device__ inline uint32_t ring5_row(uint32_t pos, uint32_t off) {
-  return (__builtin_amdgcn_ubfe(pos, 2u, 4u) << 8) + off;    // row (pos / 4) mod 16
+  // row (pos / 4) mod 16: one bit-field extract and one shift-add (opaque
+  // keeps the compiler from turning the extract into a shift and a mask)
+  return (opaque(__builtin_amdgcn_ubfe(pos, 2u, 4u)) << 8) + off;
 }
 
 // Writes the 16-byte chunk at frame position pos (a multiple of 16, so its
