@@ -25,6 +25,7 @@
 // v_mad_u32_u24 per symbol), a 64-byte ring per lane refilled by 16-byte loads
 // two 16-symbol blocks ahead, and an fp16 V chunk.
 
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -970,6 +971,39 @@ __device__ inline uint32_t dword_of(const uint4 (&v)[N], int i) {
   return (i % 4 == 0) ? q.x : (i % 4 == 1) ? q.y : (i % 4 == 2) ? q.z : q.w;
 }
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1, fully unrolled.
+template <int B, int E>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F& f) {
+    if constexpr (B < E) {
+      f(std::integral_constant<int, B>{});
+      StaticFor<B + 1, E>::run(f);
+    }
+  }
+};
+
+// One lane's K and V bit vectors of KV head g of token t, and the head's query
+// operand in the broadcast layout (register r holds channel quad 16 r + the
+// lane's MFMA block).
+template <int KQ, int VQ, int NGM>
+__device__ __forceinline__ void fw_fetch(uint4 (&kd)[KQ], uint4 (&vd)[VQ], uint4 (&qd)[NGM][2],
+                                         const Attn2Args& a, int64_t s, int64_t t, int g, int lane,
+                                         const uint4* qop, int qn) {
+  const int64_t rw = s * a.T_cap + t + lane;
+  const uint4* kr = reinterpret_cast<const uint4*>(a.k_cont + rw * a.CK) + g * KQ;
+  const uint4* vr = reinterpret_cast<const uint4*>(a.v_cont + rw * a.CV) + g * VQ;
+#pragma unroll
+  for (int j = 0; j < KQ; ++j) kd[j] = kr[j];
+#pragma unroll
+  for (int j = 0; j < VQ; ++j) vd[j] = vr[j];
+  const uint4* qg = qop + g * (NGM * 32 * 4) + qn;
+#pragma unroll
+  for (int m = 0; m < NGM; ++m)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) qd[m][r] = qg[(m * 32 + 16 * r + (lane >> 2)) * 4];
+}
+
 template <int G, int HKV, int BK, int BV>
 __global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
   constexpr int HQ = G * HKV;
@@ -999,6 +1033,9 @@ __global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
   const uint32_t lutHiV = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
   wave_lds_fence();
 
+  // Output accumulators, rotated once per head step (as in the entropy-coded
+  // kernel) so the loop over heads needs no register indexing: during head g's
+  // step O[0] holds head g, and after the last head O[j] holds head j again.
   float4_t O[HKV][2][NGM];
 #pragma unroll
   for (int g = 0; g < HKV; ++g)
@@ -1015,6 +1052,18 @@ __global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
   const float* qmu = a.qmu + s * HQ * a.nW;
   const int qn = lane & 3;
 
+  // Per head, one lane's whole K and V bit vectors (KW and VW dwords) and the
+  // query operand are registers, fetched one head ahead (the next tile's first
+  // head after the last), so no load is waited for inside a head.  The query
+  // operand of channel quad c lives in register c / 16 of the lanes of MFMA
+  // block c mod 16, which the QK^T MFMA broadcasts to all blocks (CBSZ = 4).
+  // With two MFMA groups the prefetch would not fit the registers: the head's
+  // own loads are issued at its start instead.
+  constexpr bool kPre = NGM == 1;
+  constexpr int KQ = KW / 4, VQ = VW / 4;                  // uint4 per head
+  uint4 kn[KQ], vn[VQ], qn4[NGM][2];
+  if (kPre) fw_fetch<KQ, VQ, NGM>(kn, vn, qn4, a, s, tb, 0, lane, qop, qn);
+
   for (int64_t t0 = tb; t0 < te; t0 += 64) {
     const int64_t row = s * a.T_cap + t0 + lane;
     const float sk = h2f(a.k_so[2 * row]), ok = h2f(a.k_so[2 * row + 1]);
@@ -1026,55 +1075,47 @@ __global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
       affM[h] = qmu[h * a.nW + wdx];
     }
     wave_lds_fence();
-    const uint32_t* kr = reinterpret_cast<const uint32_t*>(a.k_cont + row * a.CK);
-    const uint4* vr = reinterpret_cast<const uint4*>(a.v_cont + row * a.CV);
-#pragma unroll
+#pragma unroll 1
     for (int g = 0; g < HKV; ++g) {
-      // this head's V bits arrive while its K levels are contracted
-      uint4 vc[VW / 4];
+      uint4 kc[KQ], vc[VQ], qh[NGM][2];
+      if (kPre) {
 #pragma unroll
-      for (int j = 0; j < VW / 4; ++j) vc[j] = vr[g * (VW / 4) + j];
-      // ---- QK^T on the K levels of head g: 8 blocks of 4 channel quads, the
-      // K bits of a block (BK / 2 dwords) loaded one block ahead
+        for (int j = 0; j < KQ; ++j) kc[j] = kn[j];
+#pragma unroll
+        for (int j = 0; j < VQ; ++j) vc[j] = vn[j];
+#pragma unroll
+        for (int m = 0; m < NGM; ++m) {
+          qh[m][0] = qn4[m][0];
+          qh[m][1] = qn4[m][1];
+        }
+        // the next head of this tile, else the next tile's first (the last
+        // head of the last tile refetches the current tile: in bounds, unused)
+        const bool last = g + 1 == HKV;
+        const int64_t tn = last && t0 + 64 < te ? t0 + 64 : t0;
+        fw_fetch<KQ, VQ, NGM>(kn, vn, qn4, a, s, tn, last ? 0 : g + 1, lane, qop, qn);
+      } else {
+        fw_fetch<KQ, VQ, NGM>(kc, vc, qh, a, s, t0, g, lane, qop, qn);
+      }
+      // ---- QK^T on the K levels of head g, one MFMA pair per channel quad
       float4_t D[NGM];
 #pragma unroll
       for (int m = 0; m < NGM; ++m) D[m] = float4_t{0.f, 0.f, 0.f, 0.f};
-      const uint4* qg = qop + g * (NGM * 32 * 4) + qn;
-      const uint32_t* kh = kr + g * KW;
-      constexpr int KB = BK / 2;                               // dwords per block
-      uint32_t kb[KB];
+      // (a compile-time loop: the quad's dword, shift, register and MFMA block
+      // are all constants)
+      auto qk_quad = [&](auto cq) __attribute__((always_inline)) {
+        constexpr int c = decltype(cq)::value;
+        const uint32_t sym = (dword_of(kc, c / KPER) >> (BK * (c % KPER))) & KMASK;
+        const uint32_t hb = __builtin_amdgcn_perm(lutHiK, lutLoK, sym);
+        const half4_t B = as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu),
+                                   __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
 #pragma unroll
-      for (int j = 0; j < KB; ++j) kb[j] = kh[j];
-      uint4 qa[NGM];
-#pragma unroll
-      for (int m = 0; m < NGM; ++m) qa[m] = qg[(m * 32) * 4];
-#pragma unroll 1
-      for (int blk = 0; blk < 8; ++blk) {
-        const int bn = blk + 1 < 8 ? blk + 1 : 7;
-        uint32_t kbn[KB];
-#pragma unroll
-        for (int j = 0; j < KB; ++j) kbn[j] = kh[bn * KB + j];
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const int c = blk * 4 + cc;
-          const int cn = c + 1 < 32 ? c + 1 : 31;
-          uint4 qb[NGM];
-#pragma unroll
-          for (int m = 0; m < NGM; ++m) qb[m] = qg[(m * 32 + cn) * 4];
-          const uint32_t sym = (kb[cc / KPER] >> (BK * (cc % KPER))) & KMASK;
-          const uint32_t hb = __builtin_amdgcn_perm(lutHiK, lutLoK, sym);
-          const half4_t B = as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu),
-                                     __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
-#pragma unroll
-          for (int m = 0; m < NGM; ++m) {
-            D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(qa[m].x, qa[m].y), B, D[m], 0, 0, 0);
-            D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(qa[m].z, qa[m].w), B, D[m], 0, 0, 0);
-            qa[m] = qb[m];
-          }
+        for (int m = 0; m < NGM; ++m) {
+          const uint4 q4 = qh[m][c / 16];
+          D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(q4.x, q4.y), B, D[m], 4, c % 16, 0);
+          D[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(q4.z, q4.w), B, D[m], 4, c % 16, 0);
         }
-#pragma unroll
-        for (int j = 0; j < KB; ++j) kb[j] = kbn[j];
-      }
+      };
+      StaticFor<0, 32>::run(qk_quad);
       // ---- online softmax of this KV head's query heads over the tile
 #pragma unroll
       for (int v = 0; v < NW; ++v) {
@@ -1094,7 +1135,7 @@ __global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
           runL[h] = Lo * al + ls;
           runZ[h] = Zo * al + zs;
 #pragma unroll
-          for (int c = 0; c < 2; ++c) O[g][c][m][ii] *= al;
+          for (int c = 0; c < 2; ++c) O[0][c][m][ii] *= al;
           const float wt = p * sv;
           const __half hh = __float2half_rn(wt);
           whi = wt;
@@ -1128,12 +1169,24 @@ __global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
           for (int m = 0; m < NGM; ++m) {
             const uint2 ah = *reinterpret_cast<const uint2*>(&wts[0][m * 4 + qn][4 * tq]);
             const uint2 al = *reinterpret_cast<const uint2*>(&wts[1][m * 4 + qn][4 * tq]);
-            O[g][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah.x, ah.y), B, O[g][ch][m], 0, 0, 0);
-            O[g][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[g][ch][m], 0, 0, 0);
+            O[0][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah.x, ah.y), B, O[0][ch][m], 0, 0, 0);
+            O[0][ch][m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[0][ch][m], 0, 0, 0);
           }
         }
       }
       wave_lds_fence();
+      // rotate: the next head's accumulators become O[0]
+      if (HKV > 1) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int m = 0; m < NGM; ++m) {
+            const float4_t t = O[0][c][m];
+#pragma unroll
+            for (int j = 0; j + 1 < HKV; ++j) O[j][c][m] = O[j + 1][c][m];
+            O[HKV - 1][c][m] = t;
+          }
+      }
     }
   }
 
