@@ -86,7 +86,7 @@ def compare_cache(c, stats, refs, p, S):
     assert stats.cpu().numpy().astype(np.uint64).tolist() == tot.tolist()
 
 
-def run_case(name, budget_idx, seqs, tokens, w=None, levels=(8, 6), values=(None, None)):
+def run_case(name, budget_idx, seqs, tokens, w=None, levels=(8, 6), values=(None, None), mutate=None):
     kvq = _kvq()
     w = w or synth.WORKLOADS[name]
     ck, cv = w.containers[budget_idx]
@@ -97,6 +97,8 @@ def run_case(name, budget_idx, seqs, tokens, w=None, levels=(8, 6), values=(None
     p = O.OracleParams(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4, values_k=values[0],
                        values_v=values[1])
     k, v = synth.cache_inputs(w, "cuda", seqs, tokens)
+    if mutate is not None:
+        mutate(k, v)
     q = synth.queries(w, "cuda", seqs)
     c, stats = gpu_encode(kvq, plan, k, v)
     say("  gpu encode done")
@@ -173,3 +175,23 @@ def test_non_affine_levels(levels, values, cont):
     # [D-Quant] Appendix A: table entries carry arbitrary reconstruction levels
     w = synth.Workload("levels", 32, 8, 128, 2, 1, 640, 41, "keymeans", (cont,), (0.0,))
     run_case(None, 0, [0, 1], None, w=w, levels=levels, values=values)
+
+
+def test_degenerate_streams():
+    """Streams the method treats specially, on the gqa layout:
+    * an all-zero key and value window: the key mean is 0, so every stream in it
+      is constant, its grid has s = 0 and drift keeps the cheapest symbol;
+    * isolated zero value tokens;
+    * a token 1000 times larger than its neighbours (its own grid; it dominates
+      its key-mean window and, through its logits, the softmax);
+    * a key token equal to one number everywhere (a single non-zero coefficient
+      per head after the rotation)."""
+    def mutate(k, v):
+        k[0, 128:256] = 0
+        v[0, 128:256] = 0
+        v[1, 5] = 0
+        v[1, 300:310] = 0
+        k[1, 17] *= 1000
+        v[1, 17] *= 1000
+        k[0, 400] = 3.0
+    run_case("gqa", 0, [0, 1], (0, 512), mutate=mutate)
