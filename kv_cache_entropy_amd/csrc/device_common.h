@@ -60,10 +60,7 @@ struct EncShared {
   float level[kMaxLevels];
   uint32_t rate_fx[kMaxLevels];
   float rate_f[kMaxLevels];
-  uint32_t freq[kMaxLevels];
-  uint32_t cum[kMaxLevels];
-  uint32_t rcp[kMaxLevels];
-  uint32_t rshift[kMaxLevels];
+  uint4 coder[kMaxLevels];    // per symbol: (f, c, reciprocal, shift), one 16-byte read
   uint32_t cheapest;
   uint64_t budget_fx;
 };

@@ -357,26 +357,32 @@ __device__ void refit(const float (&x)[NPL], const uint8_t (&m)[NPL], float s, f
 
 // rANS encoder of one stream (one lane): symbols sym[0..n), from the last to
 // the first; pushed bytes are written downwards from img[C-1], then moved to
-// follow the 4-byte state.  Returns false if the stream would overrun.
+// follow the 4-byte state.  Returns false if the stream would overrun.  The
+// symbols are read four at a time and each symbol's coder entry is one
+// 16-byte LDS read, so only the state update is on the dependent chain.
 __device__ bool rans_encode_lane(const uint8_t* sym, int n, uint8_t* img, int C, const EncShared& sh) {
   uint32_t x = kStateLow;
   int k = 0;
   bool ok = true;
-  for (int i = n - 1; i >= 0; --i) {
-    const int mm = sym[i];
-    const uint32_t f = sh.freq[mm];
-    if (x >= (f << 23)) {
-      if (k < C - 4) {
-        img[C - 1 - k] = uint8_t(x & 0xFF);
-        ++k;
-      } else {
-        ok = false;
+  const uint32_t* sym4 = reinterpret_cast<const uint32_t*>(sym);    // n is a multiple of 4
+  for (int i4 = n / 4 - 1; i4 >= 0; --i4) {
+    const uint32_t s4 = sym4[i4];
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      const uint4 e = sh.coder[(s4 >> (8 * j)) & 0xFFu];
+      const uint32_t f = e.x;
+      if (x >= (f << 23)) {
+        if (k < C - 4) {
+          img[C - 1 - k] = uint8_t(x & 0xFF);
+          ++k;
+        } else {
+          ok = false;
+        }
+        x >>= 8;
       }
-      x >>= 8;
+      const uint32_t q = e.z ? (__umulhi(x, e.z) >> e.w) : (x >> e.w);
+      x = (q << 8) + (x - q * f) + e.y;
     }
-    const uint32_t rcp = sh.rcp[mm];
-    const uint32_t q = rcp ? (__umulhi(x, rcp) >> sh.rshift[mm]) : (x >> sh.rshift[mm]);
-    x = (q << 8) + (x - q * f) + sh.cum[mm];
   }
   img[0] = uint8_t(x);
   img[1] = uint8_t(x >> 8);
@@ -411,10 +417,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     sh.level[tid] = a.tabs.level[tid];
     sh.rate_fx[tid] = a.tabs.rate_fx[tid];
     sh.rate_f[tid] = float(a.tabs.rate_fx[tid]) * (1.0f / 65536.0f);
-    sh.freq[tid] = a.tabs.freq[tid];
-    sh.cum[tid] = a.tabs.cum[tid];
-    sh.rcp[tid] = a.tabs.rcp[tid];
-    sh.rshift[tid] = a.tabs.rshift[tid];
+    sh.coder[tid] = uint4{a.tabs.freq[tid], a.tabs.cum[tid], a.tabs.rcp[tid], a.tabs.rshift[tid]};
   }
   if (tid == 0) {
     sh.cheapest = a.tabs.cheapest;
