@@ -691,7 +691,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // decode tables, shared by the workgroup
-  for (int idx = tid; idx < 256 * int(Lay::REPS); idx += 64 * kWaves) {
+  for (int idx = tid; idx < 256 * int(Lay::REPS); idx += int(blockDim.x)) {
     const uint32_t z = uint32_t(idx) / Lay::REPS;
     uint32_t mk = 0, mv = 0;
     for (int m = 1; m < a.Mk; ++m) mk = (z >= a.ck[m]) ? uint32_t(m) : mk;
@@ -701,7 +701,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   }
   __syncthreads();
 
-  const int64_t gw = int64_t(blockIdx.x) * kWaves + w;
+  // a workgroup has up to kWaves waves (fewer when the launch is small, to
+  // spread it over more CUs); wave w of workgroup b owns split-wave b * wpw + w
+  const int64_t gw = int64_t(blockIdx.x) * (blockDim.x >> 6) + w;
   if (gw >= S * a.nsplit) return;          // (no workgroup barrier follows)
   const int64_t s = gw / a.nsplit;
   const int split = int(gw - s * a.nsplit);
@@ -1236,8 +1238,14 @@ static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stre
   // an 8-entry lookup, so it serves V alphabets of up to 8 levels
   if (a.Mv <= 8) {
     const int64_t waves = S * a.nsplit;
-    hipLaunchKernelGGL((attention4_kernel<G, HKV>), dim3(unsigned((waves + kWaves - 1) / kWaves)),
-                       dim3(64 * kWaves), 0, stream, a, S);
+    // One workgroup per CU at a time (its LDS is sized for kWaves waves): a
+    // launch too small to give every CU kWaves waves uses fewer waves per
+    // workgroup and more workgroups.
+    constexpr int64_t kCUs = 256;
+    int64_t wpw = (waves + kCUs - 1) / kCUs;
+    wpw = wpw < 1 ? 1 : (wpw > kWaves ? kWaves : wpw);
+    hipLaunchKernelGGL((attention4_kernel<G, HKV>), dim3(unsigned((waves + wpw - 1) / wpw)),
+                       dim3(unsigned(64 * wpw)), 0, stream, a, S);
   }
   else
     hipLaunchKernelGGL((attention2_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
