@@ -66,3 +66,24 @@ def test_nearest_rounding_error_bound():
     bound = np.broadcast_to(s / 2 * (1 + 1e-3) + 1e-6, x.shape)
     # inside the grid every value is within half a step of its level
     assert np.all(np.abs(x - rec)[inside] <= bound[inside])
+
+
+def test_cache_fw_equals_entropy_pipeline_without_budget_pressure():
+    # The whole-cache comparator (rotation, key means, streams) against the
+    # entropy-coded pipeline with containers too large for drift to act: the
+    # two share every step but the coding, so their symbols, metadata and key
+    # means must agree exactly.
+    rng = np.random.default_rng(8)
+    T, Hkv, d = 256, 1, 128
+    mu = rng.normal(0, 0.5, Hkv * d).astype(np.float32)
+    k = (rng.standard_normal((T, Hkv * d)) + mu).astype(np.float32)
+    v = rng.standard_normal((T, Hkv * d)).astype(np.float32)
+    fw = O.encode_cache_fw(k, v, Hkv, d, 6, 3, 128)
+    ent = O.encode_cache(k, v, O.OracleParams(Hkv, d, 6, 3, 200, 200, 128, 1.4))
+    for key in ("k_sym", "v_sym", "k_mean_q"):
+        assert np.array_equal(fw[key], ent[key]), key
+    for key in ("k_so", "v_so", "k_mean_scale"):
+        assert np.array_equal(np.asarray(fw[key]).view(np.uint16), np.asarray(ent[key]).view(np.uint16)), key
+    assert fw["k_cont"].shape == (T, O.fw_container_bytes(6, Hkv * d))
+    assert np.array_equal(O.fw_unpack(fw["k_cont"], 6, Hkv * d), fw["k_sym"])
+    assert np.array_equal(O.fw_unpack(fw["v_cont"], 3, Hkv * d), fw["v_sym"])
