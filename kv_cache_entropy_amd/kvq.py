@@ -87,14 +87,44 @@ def _check(fn, status):
         raise KvqError(fn, status)
 
 
-def _ptr(t):
+def _ptr(t, need=None, name="tensor"):
+    """Device pointer of a contiguous GPU tensor holding at least `need` bytes.
+    The C ABI takes bare pointers, so this is the only place where a host
+    tensor or a short buffer can be caught before a kernel touches it."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
-        raise TypeError("expected a torch tensor")
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
     if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
+        raise ValueError(f"{name}: must be contiguous")
+    if need is not None and t.numel() * t.element_size() < need:
+        raise ValueError(f"{name}: holds {t.numel() * t.element_size()} bytes, needs {need}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _cache_ptrs(plan, S, rows, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale):
+    """Pointers of the six cache arrays for S sequences of `rows` token rows."""
+    p = plan.params
+    nW = rows // p.mean_window
+    return (_ptr(k_cont, S * rows * p.container_bytes_k, "k_cont"),
+            _ptr(v_cont, S * rows * p.container_bytes_v, "v_cont"),
+            _ptr(k_so, S * rows * 4, "k_so"), _ptr(v_so, S * rows * 4, "v_so"),
+            _ptr(k_mean_q, S * nW * plan.n, "k_mean_q"), _ptr(k_mean_scale, S * nW * 2, "k_mean_scale"))
+
+
+def _kv_ptrs(plan, k, v):
+    """(dtype code, S, T, k pointer, v pointer) of K/V inputs [S, T, Hkv, d] or [S, T, n]."""
+    if k.dtype != v.dtype or k.shape != v.shape:
+        raise ValueError("k and v must have the same dtype and shape")
+    dt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}.get(k.dtype)
+    if dt is None:
+        raise TypeError("k/v must be float32 or bfloat16")
+    S, T = int(k.shape[0]), int(k.shape[1])
+    if k.numel() != S * T * plan.n:
+        raise ValueError(f"k/v must hold [S, T, {plan.n}] values")
+    return dt, S, T, _ptr(k, name="k"), _ptr(v, name="v")
 
 
 def _stream(stream):
@@ -177,15 +207,10 @@ def kvq_containers_for_budget(bits_per_elem, n_kv_heads, head_dim, mean_window):
 def kvq_encode_streams(plan, k, v, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale,
                        stats=None, stream=None):
     """k, v: [S, T, Hkv, d] (or [S, T, n]) fp32/bf16 CUDA tensors; outputs as in kvq.h."""
-    if k.dtype != v.dtype or k.shape != v.shape:
-        raise ValueError("k and v must have the same dtype and shape")
-    dt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}.get(k.dtype)
-    if dt is None:
-        raise TypeError("k/v must be float32 or bfloat16")
-    S, T = int(k.shape[0]), int(k.shape[1])
+    dt, S, T, kp, vp = _kv_ptrs(plan, k, v)
+    cp = _cache_ptrs(plan, S, T, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale)
     _check("kvq_encode_streams", lib().kvq_encode_streams(
-        plan.handle, _ptr(k), _ptr(v), dt, S, T, _ptr(k_cont), _ptr(v_cont), _ptr(k_so),
-        _ptr(v_so), _ptr(k_mean_q), _ptr(k_mean_scale), _ptr(stats), _stream(stream)))
+        plan.handle, kp, vp, dt, S, T, *cp, _ptr(stats, 64, "stats"), _stream(stream)))
 
 
 def kvq_decode_attention(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, out,
@@ -195,26 +220,24 @@ def kvq_decode_attention(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_s
         raise TypeError("q and out must be bfloat16")
     S, Hq = int(q.shape[0]), int(q.shape[1])
     T = int(k_cont.shape[1])
+    d = plan.params.head_dim
+    cp = _cache_ptrs(plan, S, T, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale)
     _check("kvq_decode_attention", lib().kvq_decode_attention(
-        plan.handle, _ptr(q), Hq, _ptr(k_cont), _ptr(v_cont), _ptr(k_so), _ptr(v_so),
-        _ptr(k_mean_q), _ptr(k_mean_scale), S, T, float(softmax_scale), _ptr(out), _ptr(out_f32),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        plan.handle, _ptr(q, S * Hq * d * 2, "q"), Hq, *cp, S, T, float(softmax_scale),
+        _ptr(out, S * Hq * d * 2, "out"), _ptr(out_f32, S * Hq * d * 4, "out_f32"),
+        _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def kvq_encode_append(plan, k, v, cache, token_offset, stats=None, stream=None):
     """Encodes k, v [S, T', Hkv, d] into rows [token_offset, token_offset + T') of `cache`
     (the dict of alloc_cache, whose second dimension is the capacity)."""
-    if k.dtype != v.dtype or k.shape != v.shape:
-        raise ValueError("k and v must have the same dtype and shape")
-    dt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}.get(k.dtype)
-    if dt is None:
-        raise TypeError("k/v must be float32 or bfloat16")
-    S, T = int(k.shape[0]), int(k.shape[1])
+    dt, S, T, kp, vp = _kv_ptrs(plan, k, v)
     cap = int(cache["k_cont"].shape[1])
+    cp = _cache_ptrs(plan, S, cap, cache["k_cont"], cache["v_cont"], cache["k_so"], cache["v_so"],
+                     cache["k_mean_q"], cache["k_mean_scale"])
     _check("kvq_encode_append", lib().kvq_encode_append(
-        plan.handle, _ptr(k), _ptr(v), dt, S, T, cap, int(token_offset), _ptr(cache["k_cont"]),
-        _ptr(cache["v_cont"]), _ptr(cache["k_so"]), _ptr(cache["v_so"]), _ptr(cache["k_mean_q"]),
-        _ptr(cache["k_mean_scale"]), _ptr(stats), _stream(stream)))
+        plan.handle, kp, vp, dt, S, T, cap, int(token_offset), *cp, _ptr(stats, 64, "stats"),
+        _stream(stream)))
 
 
 def kvq_decode_attention_ex(plan, q, cache, n_tokens, res_k, res_v, res_len, out, workspace,
@@ -230,11 +253,15 @@ def kvq_decode_attention_ex(plan, q, cache, n_tokens, res_k, res_v, res_len, out
     rcap = int(res_k.shape[1]) if res_k is not None else 0
     if res_k is not None and (res_k.dtype != torch.bfloat16 or res_v.dtype != torch.bfloat16):
         raise TypeError("res_k and res_v must be bfloat16")
+    d = plan.params.head_dim
+    cp = _cache_ptrs(plan, S, cap, c.get("k_cont"), c.get("v_cont"), c.get("k_so"), c.get("v_so"),
+                     c.get("k_mean_q"), c.get("k_mean_scale"))
+    rbytes = S * rcap * plan.n * 2
     _check("kvq_decode_attention_ex", lib().kvq_decode_attention_ex(
-        plan.handle, _ptr(q), Hq, _ptr(c.get("k_cont")), _ptr(c.get("v_cont")), _ptr(c.get("k_so")),
-        _ptr(c.get("v_so")), _ptr(c.get("k_mean_q")), _ptr(c.get("k_mean_scale")), S, cap,
-        int(n_tokens), _ptr(res_k), _ptr(res_v), rcap, int(res_len), float(softmax_scale), _ptr(out),
-        _ptr(out_f32), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        plan.handle, _ptr(q, S * Hq * d * 2, "q"), Hq, *cp, S, cap, int(n_tokens),
+        _ptr(res_k, rbytes, "res_k"), _ptr(res_v, rbytes, "res_v"), rcap, int(res_len),
+        float(softmax_scale), _ptr(out, S * Hq * d * 2, "out"), _ptr(out_f32, S * Hq * d * 4, "out_f32"),
+        _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def kvq_fixed_width_container_bytes(levels, n):
@@ -245,15 +272,10 @@ def kvq_fixed_width_container_bytes(levels, n):
 
 def kvq_encode_fixed_width(plan, k, v, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, stream=None):
     """As kvq_encode_streams, in the fixed-width comparator format."""
-    if k.dtype != v.dtype or k.shape != v.shape:
-        raise ValueError("k and v must have the same dtype and shape")
-    dt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}.get(k.dtype)
-    if dt is None:
-        raise TypeError("k/v must be float32 or bfloat16")
-    S, T = int(k.shape[0]), int(k.shape[1])
+    dt, S, T, kp, vp = _kv_ptrs(plan, k, v)
+    cp = _cache_ptrs(plan, S, T, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale)
     _check("kvq_encode_fixed_width", lib().kvq_encode_fixed_width(
-        plan.handle, _ptr(k), _ptr(v), dt, S, T, _ptr(k_cont), _ptr(v_cont), _ptr(k_so),
-        _ptr(v_so), _ptr(k_mean_q), _ptr(k_mean_scale), _stream(stream)))
+        plan.handle, kp, vp, dt, S, T, *cp, _stream(stream)))
 
 
 def kvq_decode_attention_fixed_width(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, out,
@@ -263,17 +285,23 @@ def kvq_decode_attention_fixed_width(plan, q, k_cont, v_cont, k_so, v_so, k_mean
         raise TypeError("q and out must be bfloat16")
     S, Hq = int(q.shape[0]), int(q.shape[1])
     T = int(k_cont.shape[1])
+    d = plan.params.head_dim
+    cp = _cache_ptrs(plan, S, T, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale)
     _check("kvq_decode_attention_fixed_width", lib().kvq_decode_attention_fixed_width(
-        plan.handle, _ptr(q), Hq, _ptr(k_cont), _ptr(v_cont), _ptr(k_so), _ptr(v_so),
-        _ptr(k_mean_q), _ptr(k_mean_scale), S, T, float(softmax_scale), _ptr(out), _ptr(out_f32),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        plan.handle, _ptr(q, S * Hq * d * 2, "q"), Hq, *cp, S, T, float(softmax_scale),
+        _ptr(out, S * Hq * d * 2, "out"), _ptr(out_f32, S * Hq * d * 4, "out_f32"),
+        _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def kvq_decode_symbols(plan, side, cont, symbols, end_ok=None, stream=None):
     """cont: [..., C] uint8; symbols: [..., n] uint8; end_ok: nullable int32/uint32-sized."""
-    n_streams = cont.numel() // cont.shape[-1]
+    C = plan.params.container_bytes_k if side == 0 else plan.params.container_bytes_v
+    if cont.shape[-1] != C:
+        raise ValueError(f"cont: last dimension must be the container size {C}")
+    n_streams = cont.numel() // C
     _check("kvq_decode_symbols", lib().kvq_decode_symbols(
-        plan.handle, side, _ptr(cont), n_streams, _ptr(symbols), _ptr(end_ok), _stream(stream)))
+        plan.handle, side, _ptr(cont, name="cont"), n_streams, _ptr(symbols, n_streams * plan.n, "symbols"),
+        _ptr(end_ok, n_streams * 4, "end_ok"), _stream(stream)))
 
 
 def kvq_timing_enable(on):

@@ -179,3 +179,20 @@ def test_planner_rejects_bad_levels():
         with pytest.raises(kvq.KvqError) as e:
             kvq.Plan(8, 128, 4, 6, 331, 231, values_k=vk)
         assert e.value.status == -1
+
+
+def test_binding_rejects_host_tensors_and_short_buffers():
+    """The C ABI takes bare device pointers; the binding refuses host tensors
+    (a kernel would fault on them) before anything reaches the library."""
+    import torch
+    from kv_cache_entropy_amd import kvq
+    plan = kvq.Plan(2, 128, 8, 6, 90, 62, 128, 1.4)
+    k = torch.zeros(1, 128, 256, dtype=torch.bfloat16)
+    c = {key: torch.zeros(4, dtype=torch.uint8) for key in
+         ("k_cont", "v_cont", "k_so", "v_so", "k_mean_q", "k_mean_scale")}
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kvq.kvq_encode_streams(plan, k, k, *c.values())
+    with pytest.raises(ValueError, match="k/v must hold"):
+        kvq.kvq_encode_streams(plan, k[:, :, :128], k[:, :, :128], *c.values())
+    with pytest.raises(ValueError, match="container size"):
+        kvq.kvq_decode_symbols(plan, 0, torch.zeros(3, 91, dtype=torch.uint8), torch.zeros(3, 256, dtype=torch.uint8))
