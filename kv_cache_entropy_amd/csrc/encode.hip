@@ -371,17 +371,20 @@ __device__ bool rans_encode_lane(const uint8_t* sym, int n, uint8_t* img, int C,
     for (int j = 3; j >= 0; --j) {
       const uint4 e = sh.coder[(s4 >> (8 * j)) & 0xFFu];
       const uint32_t f = e.x;
-      if (x >= (f << 23)) {
-        if (k < C - 4) {
-          img[C - 1 - k] = uint8_t(x & 0xFF);
-          ++k;
-        } else {
-          ok = false;
-        }
-        x >>= 8;
-      }
+      // Branch-free renormalisation: the low byte is always stored at the
+      // next push position and only counted when it is pushed (an uncounted
+      // byte is overwritten by the next push, or lies outside the payload
+      // that the tail below keeps).  At most one byte per symbol: afterwards
+      // x < f 2^23.
+      const bool rn = x >= (f << 23);
+      img[C - 1 - k] = uint8_t(x & 0xFF);
+      ok = ok && !(rn && k >= C - 4);
+      k += (rn && k < C - 4) ? 1 : 0;
+      x = rn ? (x >> 8) : x;
+      // q = x / f (exact; see the planner), q < 2^23 and f < 2^8, so the
+      // product is a 24-bit multiply
       const uint32_t q = e.z ? (__umulhi(x, e.z) >> e.w) : (x >> e.w);
-      x = (q << 8) + (x - q * f) + e.y;
+      x = (q << 8) + (x - __umul24(q, f)) + e.y;
     }
   }
   img[0] = uint8_t(x);
