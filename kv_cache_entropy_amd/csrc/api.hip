@@ -92,9 +92,12 @@ int fw_bits(int levels) {
 // Streams per encode workgroup: the largest of 32/16/8/4 that divides the
 // tokens per sequence (a workgroup's streams then lie in one sequence) and
 // keeps the symbol and container staging under 56 KiB.
+// Streams per encode workgroup: as many as fit (symbols staged at 4 bits,
+// plus the container image) in 56 KiB of LDS, up to one per lane of a wave,
+// since one lane per stream runs the rANS phase.
 int pick_spw(int64_t tokens, int n, int C) {
-  for (int spw = 32; spw >= 4; spw >>= 1)
-    if (tokens % spw == 0 && size_t(spw) * (size_t(n) + size_t(C)) <= 56u * 1024u) return spw;
+  for (int spw = 64; spw >= 4; spw >>= 1)
+    if (tokens % spw == 0 && size_t(spw) * (size_t(n) / 2 + size_t(C)) <= 56u * 1024u) return spw;
   return 0;
 }
 

@@ -355,21 +355,22 @@ __device__ void refit(const float (&x)[NPL], const uint8_t (&m)[NPL], float s, f
   o16 = __float2half_rn(float(on));
 }
 
-// rANS encoder of one stream (one lane): symbols sym[0..n), from the last to
-// the first; pushed bytes are written downwards from img[C-1], then moved to
-// follow the 4-byte state.  Returns false if the stream would overrun.  The
-// symbols are read four at a time and each symbol's coder entry is one
-// 16-byte LDS read, so only the state update is on the dependent chain.
+// rANS encoder of one stream (one lane): symbols sym[0..n) packed two per
+// byte (symbol i in nibble i mod 2 of byte i / 2), from the last to the first;
+// pushed bytes are written downwards from img[C-1], then moved to follow the
+// 4-byte state.  Returns false if the stream would overrun.  The symbols are
+// read eight at a time and each symbol's coder entry is one 16-byte LDS read,
+// so only the state update is on the dependent chain.
 __device__ bool rans_encode_lane(const uint8_t* sym, int n, uint8_t* img, int C, const EncShared& sh) {
   uint32_t x = kStateLow;
   int k = 0;
   bool ok = true;
-  const uint32_t* sym4 = reinterpret_cast<const uint32_t*>(sym);    // n is a multiple of 4
-  for (int i4 = n / 4 - 1; i4 >= 0; --i4) {
-    const uint32_t s4 = sym4[i4];
+  const uint32_t* sym8 = reinterpret_cast<const uint32_t*>(sym);    // n is a multiple of 8
+  for (int i8 = n / 8 - 1; i8 >= 0; --i8) {
+    const uint32_t s8 = sym8[i8];
 #pragma unroll
-    for (int j = 3; j >= 0; --j) {
-      const uint4 e = sh.coder[(s4 >> (8 * j)) & 0xFFu];
+    for (int j = 7; j >= 0; --j) {
+      const uint4 e = sh.coder[(s8 >> (4 * j)) & 0xFu];
       const uint32_t f = e.x;
       // Branch-free renormalisation: the low byte is always stored at the
       // next push position and only counted when it is pushed (an uncounted
@@ -413,8 +414,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int SPW = a.spw;
   const int n = a.n, C = a.tabs.container_bytes, M = a.tabs.levels;
-  uint8_t* sym = dyn;                      // [SPW][n]
-  uint8_t* img = dyn + size_t(SPW) * n;    // [SPW][C]
+  uint8_t* sym = dyn;                          // [SPW][n / 2]: two 4-bit symbols per byte
+  uint8_t* img = dyn + size_t(SPW) * (n / 2);  // [SPW][C]
   for (int i = tid; i < 512; i += 256) sh.lambda[i] = a.tabs.lambda[i];
   if (tid < kMaxLevels) {
     sh.level[tid] = a.tabs.level[tid];
@@ -474,9 +475,15 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 #pragma unroll
       for (int i = 0; i < NPL; ++i) ch += (m[i] != near[i]) ? 1u : 0u;
       changed += wave_sum_u32(ch);
-      uint8_t* dst = sym + size_t(sl) * n + size_t(lane) * NPL;
+      // symbols i = lane NPL + idx, two per byte (levels <= 16)
+      if constexpr (NPL >= 2) {
+        uint8_t* dst = sym + size_t(sl) * (n / 2) + size_t(lane) * (NPL / 2);
 #pragma unroll
-      for (int i = 0; i < NPL; ++i) dst[i] = m[i];
+        for (int b = 0; b < NPL / 2; ++b) dst[b] = uint8_t(m[2 * b] | (m[2 * b + 1] << 4));
+      } else {
+        const uint32_t odd = __shfl_xor(uint32_t(m[0]), 1, 64);
+        if (!(lane & 1)) sym[size_t(sl) * (n / 2) + size_t(lane / 2)] = uint8_t(m[0] | (odd << 4));
+      }
     }
     if (lane == 0) so_sh[sl] = uint32_t(__half_as_ushort(s16)) | (uint32_t(__half_as_ushort(o16)) << 16);
   }
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   uint32_t overrun = 0;
   if (tid < SPW) {
     if constexpr (!FW)
-      overrun = rans_encode_lane(sym + size_t(tid) * n, n, img + size_t(tid) * C, C, sh) ? 0u : 1u;
+      overrun = rans_encode_lane(sym + size_t(tid) * (n / 2), n, img + size_t(tid) * C, C, sh) ? 0u : 1u;
     reinterpret_cast<uint32_t*>(a.so)[ost0 + tid] = so_sh[tid];
   }
   __syncthreads();
@@ -517,7 +524,7 @@ hipError_t launch_key_mean(const KeyMeanArgs& a, int64_t n_windows, hipStream_t 
 }
 
 hipError_t launch_encode(const EncodeArgs& a, int64_t n_streams, hipStream_t stream) {
-  const size_t lds = size_t(a.spw) * (size_t(a.n) + size_t(a.tabs.container_bytes));
+  const size_t lds = size_t(a.spw) * (size_t(a.n) / 2 + size_t(a.tabs.container_bytes));
   const dim3 grid(unsigned(n_streams / a.spw)), block(256);
   if (a.fw_bits) {
     const int key = (a.n / 64) * 16 + a.fw_bits;
