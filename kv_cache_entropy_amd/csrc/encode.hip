@@ -79,6 +79,24 @@ __global__ __launch_bounds__(1024) void key_mean_kernel(KeyMeanArgs a) {
   if (tid == 0) a.mean_scale[orow] = __half_as_ushort(sc16);
 }
 
+// Wave-wide integer sum in VALU only (DPP within rows of 16 lanes, then the
+// gfx950 row and half-wave swaps): no LDS round trips on the drift's
+// per-step critical path.  Integer addition, so the order does not matter.
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline uint32_t wave_sum_u32_dpp(uint32_t v) {
+  v += dpp_u32<0xB1>(v);      // quad_perm [1,0,3,2]
+  v += dpp_u32<0x4E>(v);      // quad_perm [2,3,0,1]
+  v += dpp_u32<0x124>(v);     // row_ror:4
+  v += dpp_u32<0x128>(v);     // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const uint32_t r = a[0] + a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(r, r, false, false);
+  return __builtin_amdgcn_readfirstlane(b[0] + b[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Drift (Algorithm 1) for the stream held NPL values per lane by one wave.
 // Returns true if the encoder fell back to the cheapest symbol everywhere.
@@ -164,7 +182,7 @@ __device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& 
     uint32_t R = 0;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) R += sh.rate_fx[cur[i]];
-    R = wave_sum_u32(R);
+    R = wave_sum_u32_dpp(R);
     const bool ok = uint64_t(R) <= sh.budget_fx;
     if (step < 12) {
       if (ok) {
@@ -251,7 +269,7 @@ __device__ bool drift_large(const float (&x)[NPL], float s, float o, const EncSh
     uint32_t R = 0;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) R += sh.rate_fx[cur[i]];
-    R = wave_sum_u32(R);
+    R = wave_sum_u32_dpp(R);
     const bool ok = uint64_t(R) <= sh.budget_fx;
     if (step < 12) {
       if (ok) {
