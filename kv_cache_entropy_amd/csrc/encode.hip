@@ -97,6 +97,30 @@ __device__ inline uint32_t wave_sum_u32_dpp(uint32_t v) {
   return __builtin_amdgcn_readfirstlane(b[0] + b[1]);
 }
 
+// Wave-wide max / min of finite floats, in VALU only, on order-preserving
+// integer keys (sign-folded bit patterns): the result is the same value
+// whatever the reduction order.  Lanes a DPP pattern leaves without a source
+// would keep the identity (every pattern used is a full permutation).
+__device__ inline int float_key(int b) { return b ^ ((b >> 31) & 0x7FFFFFFF); }
+template <int CTRL, bool MAX>
+__device__ inline int dpp_ext(int v) {
+  const int o = __builtin_amdgcn_update_dpp(MAX ? int(0x80000000) : int(0x7FFFFFFF), v, CTRL, 0xF, 0xF, false);
+  return MAX ? (v > o ? v : o) : (v < o ? v : o);
+}
+template <bool MAX>
+__device__ inline float wave_ext_dpp(float x) {
+  int k = float_key(__float_as_int(x));
+  k = dpp_ext<0xB1, MAX>(k);
+  k = dpp_ext<0x4E, MAX>(k);
+  k = dpp_ext<0x124, MAX>(k);
+  k = dpp_ext<0x128, MAX>(k);
+  const auto a = __builtin_amdgcn_permlane16_swap(uint32_t(k), uint32_t(k), false, false);
+  const int r = MAX ? (int(a[0]) > int(a[1]) ? int(a[0]) : int(a[1])) : (int(a[0]) < int(a[1]) ? int(a[0]) : int(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(uint32_t(r), uint32_t(r), false, false);
+  const int t = MAX ? (int(b[0]) > int(b[1]) ? int(b[0]) : int(b[1])) : (int(b[0]) < int(b[1]) ? int(b[0]) : int(b[1]));
+  return __int_as_float(float_key(__builtin_amdgcn_readfirstlane(t)));
+}
+
 // ---------------------------------------------------------------------------
 // Drift (Algorithm 1) for the stream held NPL values per lane by one wave.
 // Returns true if the encoder fell back to the cheapest symbol everywhere.
@@ -137,8 +161,8 @@ __device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& 
 #pragma unroll
     for (int i = 0; i < NPL; ++i) (*near)[i] = uint8_t(bl[i]);
   }
-  dmax = wave_max(dmax);
-  dmin = wave_min(dmin);
+  dmax = wave_ext_dpp<true>(dmax);
+  dmin = wave_ext_dpp<false>(dmin);
   const float y = __fmul_rn(__fsub_rn(dmax, dmin), 8.0f);
   const uint8_t cheap = uint8_t(sh.cheapest);
   if (!(y > 0.f)) {
@@ -227,8 +251,8 @@ __device__ bool drift_large(const float (&x)[NPL], float s, float o, const EncSh
 #pragma unroll
     for (int i = 0; i < NPL; ++i) (*near)[i] = bl[i];
   }
-  dmax = wave_max(dmax);
-  dmin = wave_min(dmin);
+  dmax = wave_ext_dpp<true>(dmax);
+  dmin = wave_ext_dpp<false>(dmin);
   const float y = __fmul_rn(__fsub_rn(dmax, dmin), 8.0f);
   const uint8_t cheap = uint8_t(sh.cheapest);
   if (!(y > 0.f)) {
@@ -466,8 +490,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     float mn = x[0], mx = x[0];
 #pragma unroll
     for (int i = 1; i < NPL; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-    mn = __fadd_rn(wave_min(mn), 0.0f);     // a negative zero becomes +0
-    mx = __fadd_rn(wave_max(mx), 0.0f);
+    mn = __fadd_rn(wave_ext_dpp<false>(mn), 0.0f);     // a negative zero becomes +0
+    mx = __fadd_rn(wave_ext_dpp<true>(mx), 0.0f);
     const float s = __fdiv_rn(__fsub_rn(mx, mn), float(M - 1));
     const float o = mn;
     uint8_t m[NPL];
