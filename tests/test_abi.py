@@ -196,3 +196,15 @@ def test_binding_rejects_host_tensors_and_short_buffers():
         kvq.kvq_encode_streams(plan, k[:, :, :128], k[:, :, :128], *c.values())
     with pytest.raises(ValueError, match="container size"):
         kvq.kvq_decode_symbols(plan, 0, torch.zeros(3, 91, dtype=torch.uint8), torch.zeros(3, 256, dtype=torch.uint8))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library the binding raises; nothing falls back to
+    another implementation."""
+    from kv_cache_entropy_amd import kvq
+    monkeypatch.setattr(kvq, "_lib", None)
+    monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "libkvq.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        kvq.Plan(2, 128)
+    with pytest.raises(RuntimeError, match="missing"):
+        kvq.kvq_model_probs(8, 1024)
