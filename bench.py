@@ -282,15 +282,36 @@ def main():
         import oracle as O
         from tests.oracle_pool import encode_cache_parallel, n_workers, time_decode_attention
         p = O.OracleParams(w.n_kv_heads, d, 8, 6, ck, cv, 128, 1.4)
-        refs = [encode_cache_parallel(kk, vv, p) for kk, vv in zip(base_k, base_v)]
-        procs = min(n_workers(), 8)
-        sample_bytes_one = base_tokens * (ck + cv + 8) + (base_tokens // 128) * (n + 2)
-        dt, tasks, _ = time_decode_attention(refs, base_q, p, procs, target_s=8.0)
+        # one worker process per host core, each single-threaded (no nested
+        # BLAS threads); the spawned workers inherit these settings
+        saved = {key: os.environ.get(key) for key in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                      "MKL_NUM_THREADS")}
+        for key in saved:
+            os.environ[key] = "1"
+        try:
+            refs = [encode_cache_parallel(kk, vv, p) for kk, vv in zip(base_k, base_v)]
+            procs = n_workers()
+            sample_bytes_one = base_tokens * (ck + cv + 8) + (base_tokens // 128) * (n + 2)
+            dt, tasks, _ = time_decode_attention(refs, base_q, p, procs, target_s=8.0)
+        finally:
+            for key, val in saved.items():
+                if val is None:
+                    os.environ.pop(key, None)
+                else:
+                    os.environ[key] = val
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as fh:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                                 cpu_model)
+        except OSError:
+            pass
         cpu = {"value": sample_bytes_one * tasks / dt / 1e9, "unit": "GB/s", "cores": procs,
-               "kind": "oracle",
+               "kind": "oracle", "cpu": cpu_model,
                "sample": f"{tasks} decode-attention tasks of one sequence each ({base_tokens} tokens, "
                          f"sequences {base_seqs} of this workload, all {Hq} query heads): Algorithm-2 "
-                         f"decode + float64 attention in {procs} worker processes; {dt:.1f} s wall"}
+                         f"decode + float64 attention in {procs} single-threaded worker processes; "
+                         f"{dt:.1f} s wall"}
         log(f"[bench] cpu oracle {cpu['value'] * 1e3:.3f} MB/s on {procs} cores")
 
     rec = {
