@@ -97,6 +97,10 @@ def _ptr(t, need=None, name="tensor"):
         raise TypeError(f"{name}: expected a torch tensor")
     if not t.is_cuda:
         raise ValueError(f"{name}: must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        # kernels launch on the current device and would fault on another's memory
+        raise ValueError(f"{name}: on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     if need is not None and t.numel() * t.element_size() < need:
@@ -130,6 +134,9 @@ def _kv_ptrs(plan, k, v):
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
+    elif stream.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream: on {stream.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
