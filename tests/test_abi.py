@@ -127,6 +127,25 @@ def test_append_and_residual_entry_points_reject_bad_arguments():
     assert plan.workspace_bytes(1, 2, 0, 32) > 0      # a tail-only call still needs partials
 
 
+def test_size_limits_are_rejected_before_launch():
+    """The decode attention addresses a sequence's containers with 32-bit
+    offsets and puts sequences on the grid's y axis: past those limits it
+    returns KVQ_EUNSUPPORTED (the header's stated limits) and launches nothing."""
+    L = _lib()
+    plan = kvq.Plan(8, 128)                                # 331/231-byte containers
+    p = ctypes.c_void_p
+    a16, st = p(1 << 20), p(0)
+
+    def attend(n_seqs, n_tok):
+        return L.kvq_decode_attention(plan.handle, a16, 32, a16, a16, a16, a16, a16, a16, n_seqs, n_tok, 0.0,
+                                      a16, None, a16, 1 << 62, st)
+    t_big = (2 ** 31 // 331 // 128 + 1) * 128            # first W-multiple with T * C_K >= 2^31
+    assert t_big * 331 + 16 > 2 ** 31 - 1 and (t_big - 128) * 331 + 16 <= 2 ** 31 - 1
+    assert attend(1, t_big) == -3
+    assert attend(65536, 128) == -3                       # more sequences than grid rows
+    assert attend(65536 - 1, 128 + 1) == -1               # (shape errors still come first)
+
+
 @pytest.mark.parametrize("M,n,alpha", [(8, 1024, 1.0), (6, 1024, 1.4), (8, 128, 1.0), (3, 1024, 2.0)])
 def test_model_probs_match_oracle(M, n, alpha):
     _lib()
