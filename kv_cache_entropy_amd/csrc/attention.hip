@@ -183,18 +183,20 @@ __device__ inline float wave_max_dpp(float v) {
 }
 
 // ------------------------------------------------------------------ prologue
-// One wave per (sequence, KV head, query slot v): slot v < G is query head
-// g G + v; slots up to the next multiple of 4 are zero padding.  Writes the
-// MFMA A operand (rotated query scaled by 2^e so that max |q| is in
-// [2^7, 2^8), split into fp16 hi + lo), the inverse scale, sum_j q_rot_j and
-// sum_j q_rot_j mu_w,j for every key-mean window w.
+// One wave per (sequence, KV head, query slot v, chunk of 64 key-mean
+// windows): slot v < G is query head g G + v; slots up to the next multiple
+// of 4 are zero padding.  The chunk-0 wave writes the MFMA A operand (rotated
+// query scaled by 2^e so that max |q| is in [2^7, 2^8), split into fp16
+// hi + lo), the inverse scale and sum_j q_rot_j; every wave writes
+// sum_j q_rot_j mu_w,j for the windows w of its chunk, one per lane.
 __global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
   const int lane = threadIdx.x;
-  const int v = blockIdx.x;          // query slot in [0, NGM*4)
-  const int g = blockIdx.y;
-  const int64_t s = blockIdx.z;
   const int hkv = a.Hq / a.G;
   const int ngm = (a.G + 3) / 4;
+  const int v = int(blockIdx.x % unsigned(ngm * 4));           // query slot in [0, NGM*4)
+  const int64_t chunk = blockIdx.x / unsigned(ngm * 4);        // windows [64 chunk, 64 chunk + 64)
+  const int g = blockIdx.y;
+  const int64_t s = blockIdx.z;
   const bool real = v < a.G;
   const int h = g * a.G + v;
   float q[2] = {0.f, 0.f};
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
   const int gm = v / 4, n = v % 4;
   uint16_t* op = a.qop + ((((s * hkv + g) * ngm + gm) * 32) * 4) * 8;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 2 && chunk == 0; ++i) {
     const int j = lane * 2 + i;
     const float qs = q[i] * up;
     const __half hi = __float2half_rn(qs);
@@ -227,19 +229,20 @@ __global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
   }
   if (!real) return;
   const float qs = wave_sum_f(q[0] + q[1]);
-  if (lane == 0) {
+  if (lane == 0 && chunk == 0) {
     a.qsum[s * a.Hq + h] = qs;
     a.qscale[s * a.Hq + h] = ldexpf(1.0f, -e);
   }
-  // sum_j q_rot_j mu_w,j: one window per lane at a time, so that the windows'
-  // loads are independent (a long context has thousands of windows per head);
-  // each lane reads its window's 128 int8 means as 16-byte vectors (rows are
-  // 16-byte aligned: the base is, and n is a multiple of 128).
+  // sum_j q_rot_j mu_w,j: one window per lane, so that the windows' loads are
+  // independent (a long context has thousands of windows per head, spread
+  // over chunks); each lane reads its window's 128 int8 means as 16-byte
+  // vectors (rows are 16-byte aligned: the base is, and n is a multiple of 128).
   __shared__ float qsh[kD];
   qsh[2 * lane] = q[0];
   qsh[2 * lane + 1] = q[1];
   __syncthreads();
-  for (int64_t w = lane; w < a.nW; w += 64) {
+  const int64_t w = chunk * 64 + lane;
+  if (w < a.nW) {
     const float sc = h2f(a.mean_scale[s * a.nW_cap + w]);
     const uint4* mq = reinterpret_cast<const uint4*>(a.mean_q + (s * a.nW_cap + w) * a.n + int64_t(g) * kD);
     float acc = 0.f;
@@ -1217,7 +1220,10 @@ __global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
 
 hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t stream) {
   const int ngm = (a.G + 3) / 4;
-  hipLaunchKernelGGL(prologue2_kernel, dim3(ngm * 4, a.Hq / a.G, unsigned(S)), dim3(64), 0, stream, a);
+  const int64_t chunks = (a.nW + 63) / 64;
+  if (chunks * ngm * 4 > int64_t(0x7FFFFFFF)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prologue2_kernel, dim3(unsigned(chunks * ngm * 4), a.Hq / a.G, unsigned(S)), dim3(64), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
