@@ -56,22 +56,33 @@ __global__ __launch_bounds__(256) void decode_symbols_kernel(DecSymArgs a) {
 // merges a contiguous range (the max and per-split weights spread over the
 // lanes, the weighted sum of partial outputs over 64 splits at a time with
 // independent loads), then wave 0 merges the waves' results through LDS, undoes
-// the rotation and stores.  A single long sequence has thousands of splits.
+// the rotation and stores.  A single long sequence has thousands of splits:
+// then a first pass (FINAL = false, one workgroup per (query head, sequence,
+// group of `group` splits)) merges each group into the group's first slot, in
+// place (a group is read only by its own workgroup), and the final pass
+// merges those slots, `group` apart.
 constexpr int kCombineMaxWaves = 16;
+constexpr int kCombineGroup = 64;          // splits per first-pass workgroup
+constexpr int kCombineTwoPass = 128;       // split counts above this take two passes
 
-template <int NPL>
-__global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineArgs a) {
+template <int NPL, bool FINAL>
+__global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineArgs a, int group) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int h = blockIdx.x;
   const int64_t s = blockIdx.y;
   const int stride = a.d + 4;
-  const float* P = a.part + (s * a.nsplit) * int64_t(a.Hq) * stride + int64_t(h) * stride;
   const int64_t sp = int64_t(a.Hq) * stride;
-  const int per = (a.nsplit + nwv - 1) / nwv;
+  // the splits this workgroup merges: cnt slots, `step` apart, from `first`
+  const int first = FINAL ? 0 : int(blockIdx.z) * group;
+  const int step = FINAL ? group : 1;
+  const int cnt = FINAL ? (a.nsplit + group - 1) / group
+                        : (a.nsplit - first < group ? a.nsplit - first : group);
+  const float* P = a.part + (s * a.nsplit + first) * sp + int64_t(h) * stride;
+  const int per = (cnt + nwv - 1) / nwv;
   const int kb = wv * per;
-  const int ke = kb + per < a.nsplit ? kb + per : a.nsplit;
+  const int ke = kb + per < cnt ? kb + per : cnt;
   float Mx = -__builtin_inff();
-  for (int k = kb + lane; k < ke; k += 64) Mx = fmaxf(Mx, P[k * sp + a.d]);
+  for (int k = kb + lane; k < ke; k += 64) Mx = fmaxf(Mx, P[int64_t(k) * step * sp + a.d]);
   Mx = wave_max(Mx);
   float L = 0.f, Z = 0.f;
   float acc[NPL];
@@ -82,9 +93,10 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineA
       const int k = k0 + lane;
       float sck = 0.f, lk = 0.f, zk = 0.f;
       if (k < ke) {
-        sck = __expf(P[k * sp + a.d] - Mx);
-        lk = sck * P[k * sp + a.d + 1];
-        zk = sck * P[k * sp + a.d + 2];
+        const float* Pk = P + int64_t(k) * step * sp;
+        sck = __expf(Pk[a.d] - Mx);
+        lk = sck * Pk[a.d + 1];
+        zk = sck * Pk[a.d + 2];
       }
       L += wave_sum_f32(lk);
       Z += wave_sum_f32(zk);
@@ -93,10 +105,11 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineA
       for (int j = 0; j < kn; ++j) {
         const float sc = __shfl(sck, j, 64);
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) acc[i] += sc * P[int64_t(k0 + j) * sp + lane * NPL + i];
+        for (int i = 0; i < NPL; ++i) acc[i] += sc * P[int64_t(k0 + j) * step * sp + lane * NPL + i];
       }
     }
   }
+  float M = Mx;
   if (nwv > 1) {
     __shared__ float red[kCombineMaxWaves][64 * NPL + 4];
     if (lane == 0) {
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineA
     for (int i = 0; i < NPL; ++i) red[wv][lane * NPL + i] = acc[i];
     __syncthreads();
     if (wv != 0) return;
-    float M = -__builtin_inff();
+    M = -__builtin_inff();
     for (int w = 0; w < nwv; ++w) M = fmaxf(M, red[w][64 * NPL]);
     L = 0.f;
     Z = 0.f;
@@ -121,6 +134,18 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineA
 #pragma unroll
       for (int i = 0; i < NPL; ++i) acc[i] += sc * red[w][lane * NPL + i];
     }
+  }
+  if (!FINAL) {
+    // the merged partial replaces the group's first slot (already read)
+    float* Q = const_cast<float*>(P);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) Q[lane * NPL + i] = acc[i];
+    if (lane == 0) {
+      Q[a.d] = M;
+      Q[a.d + 1] = L;
+      Q[a.d + 2] = Z;
+    }
+    return;
   }
   const float inv = 1.0f / L;
 #pragma unroll
@@ -259,19 +284,29 @@ hipError_t launch_decode_symbols(const DecSymArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream) {
-  const dim3 grid(a.Hq, unsigned(S));
-  // about 128 splits per wave, up to 16 waves per (query head, sequence)
-  int waves = (a.nsplit + 127) / 128;
-  waves = waves < 1 ? 1 : (waves > kCombineMaxWaves ? kCombineMaxWaves : waves);
-  const dim3 block(64 * waves);
-  switch (a.d) {
-    case 64: hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+template <int NPL>
+static hipError_t launch_combine_t(const CombineArgs& a, int64_t S, hipStream_t stream) {
+  int group = 1;
+  if (a.nsplit > kCombineTwoPass) {
+    group = kCombineGroup;
+    const dim3 grid1(a.Hq, unsigned(S), unsigned((a.nsplit + group - 1) / group));
+    hipLaunchKernelGGL((combine_kernel<NPL, false>), grid1, dim3(64), 0, stream, a, group);
   }
+  // about 128 merged slots per wave, up to 16 waves per (query head, sequence)
+  const int slots = (a.nsplit + group - 1) / group;
+  int waves = (slots + 127) / 128;
+  waves = waves < 1 ? 1 : (waves > kCombineMaxWaves ? kCombineMaxWaves : waves);
+  hipLaunchKernelGGL((combine_kernel<NPL, true>), dim3(a.Hq, unsigned(S)), dim3(64 * waves), 0, stream, a, group);
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, int64_t S, hipStream_t stream) {
+  switch (a.d) {
+    case 64: return launch_combine_t<1>(a, S, stream);
+    case 128: return launch_combine_t<2>(a, S, stream);
+    case 256: return launch_combine_t<4>(a, S, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_residual(const ResidualArgs& a, int64_t S, hipStream_t stream) {

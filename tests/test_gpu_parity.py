@@ -131,7 +131,7 @@ def test_tiny_full():
     ("long", 1, [0], (1024, 1536)),
     ("long", 2, [5], (0, 512)),
     ("verylong", 0, [0], (0, 1024)),
-    ("verylong", 0, [0], (0, 8320)),    # 130 one-tile splits: the combine's split chunks, 65 windows
+    ("verylong", 0, [0], (0, 8320)),    # 130 one-tile splits: two-pass combine (groups of 64, 64, 2), 65 windows
     ("heavy", 0, [0, 7], (0, 512)),
     ("heavy", 1, [3], (0, 512)),
     ("heavy", 2, [6], (512, 1024)),
