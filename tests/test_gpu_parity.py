@@ -146,6 +146,8 @@ def test_reduced_configs(name, bi, seqs, tokens):
     (8, 1, (8, 6), (48, 36)),        # 8 query heads on one KV head (two MFMA groups)
     (8, 2, (8, 9), (96, 90)),        # 9 V levels: the non-interleaved kernel
     (4, 4, (6, 4), (150, 100)),      # other alphabets
+    (4, 4, (16, 2), (220, 68)),      # alphabet extremes: 16 key levels (drift without the
+                                     # register cache), 2 value levels with the budget met exactly
 ])
 def test_other_head_layouts_and_alphabets(hq, hkv, levels, cont):
     w = synth.Workload(f"layout{hq}x{hkv}", hq, hkv, 128, 2, 1, 640, 11 + hq + hkv, "keymeans",
