@@ -86,15 +86,16 @@ def compare_cache(c, stats, refs, p, S):
     assert stats.cpu().numpy().astype(np.uint64).tolist() == tot.tolist()
 
 
-def run_case(name, budget_idx, seqs, tokens, w=None, levels=(8, 6), values=(None, None), mutate=None):
+def run_case(name, budget_idx, seqs, tokens, w=None, levels=(8, 6), values=(None, None), mutate=None,
+             window=128):
     kvq = _kvq()
     w = w or synth.WORKLOADS[name]
     ck, cv = w.containers[budget_idx]
     mk, mv = levels
     say(f"case {w.name} budget={w.budgets[budget_idx]} C=({ck},{cv}) M=({mk},{mv}) "
-        f"heads={w.n_q_heads}/{w.n_kv_heads} seqs={seqs} tokens={tokens}")
-    plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4, values_k=values[0], values_v=values[1])
-    p = O.OracleParams(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, 128, 1.4, values_k=values[0],
+        f"heads={w.n_q_heads}/{w.n_kv_heads} seqs={seqs} tokens={tokens} W={window}")
+    plan = kvq.Plan(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, window, 1.4, values_k=values[0], values_v=values[1])
+    p = O.OracleParams(w.n_kv_heads, w.head_dim, mk, mv, ck, cv, window, 1.4, values_k=values[0],
                        values_v=values[1])
     k, v = synth.cache_inputs(w, "cuda", seqs, tokens)
     if mutate is not None:
@@ -153,6 +154,15 @@ def test_other_head_layouts_and_alphabets(hq, hkv, levels, cont):
     w = synth.Workload(f"layout{hq}x{hkv}", hq, hkv, 128, 2, 1, 640, 11 + hq + hkv, "keymeans",
                        (cont,), (0.0,))
     run_case(None, 0, [0, 1], None, w=w, levels=levels)
+
+
+@pytest.mark.parametrize("window,tokens", [(64, 640), (256, 768)])
+def test_other_key_mean_windows(window, tokens):
+    # one key mean per window of W tokens ([D-Quant] §4.5): W = 64, the smallest the
+    # attention takes (one window per tile), and W = 256 (four tiles per window)
+    w = synth.Workload(f"window{window}", 32, 8, 128, 2, 1, tokens, 53 + window // 64, "keymeans",
+                       ((331, 231),), (0.0,))
+    run_case(None, 0, [0, 1], None, w=w, window=window)
 
 
 def test_encode_is_deterministic():
