@@ -138,8 +138,9 @@ kvq_status kvq_workspace_bytes(const kvq_plan* plan, int op, int64_t n_seqs,
  *                 differ from nearest rounding on the final grid, [3] K
  *                 streams that overran their container (always 0), [4..7] the
  *                 same for V.
- * seq_len must be a positive multiple of W.  Output is deterministic and
- * independent of launch geometry. */
+ * seq_len must be a positive multiple of W.  Returns KVQ_EUNSUPPORTED unless
+ * n = Hkv d is 64 times a power of two (64 .. 4096) and W >= 4.  Output is
+ * deterministic and independent of launch geometry. */
 kvq_status kvq_encode_streams(const kvq_plan* plan, const void* k, const void* v,
                               kvq_dtype in_dtype, int64_t n_seqs, int64_t seq_len,
                               uint8_t* k_cont, uint8_t* v_cont,

@@ -191,7 +191,8 @@ kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_d
   const int W = P.mean_window;
   if (n_seqs < 1 || n_tokens < W || n_tokens % W) return KVQ_EINVAL;
   if (t_off < 0 || t_off % W || capacity % W || t_off + n_tokens > capacity) return KVQ_EINVAL;
-  if (n % 64 || n > 4096 || W < 4) return KVQ_EUNSUPPORTED;
+  // one encoder instantiation per stream length: n = 64 * 2^k up to 4096
+  if (n % 64 || n > 4096 || ((n / 64) & (n / 64 - 1)) || W < 4) return KVQ_EUNSUPPORTED;
   int fwb[2] = {0, 0};
   if (fixed_width) {
     if (!plan->side[0].affine || !plan->side[1].affine) return KVQ_EUNSUPPORTED;

@@ -127,6 +127,19 @@ def test_append_and_residual_entry_points_reject_bad_arguments():
     assert plan.workspace_bytes(1, 2, 0, 32) > 0      # a tail-only call still needs partials
 
 
+def test_encode_rejects_stream_lengths_without_a_kernel():
+    """The encoder has one instantiation per stream length n = 64 * 2^k; other
+    lengths (here 3 KV heads of 64 channels) return KVQ_EUNSUPPORTED before any
+    launch, so no output array is touched."""
+    L = _lib()
+    p = ctypes.c_void_p
+    a16, st = p(1 << 20), p(0)
+    for hkv, d, want in ((3, 64, -3), (1, 32, -3), (5, 128, -3)):
+        plan = kvq.Plan(hkv, d, 8, 6, 200, 150)
+        assert L.kvq_encode_streams(plan.handle, a16, a16, 1, 1, 128, a16, a16, a16, a16, a16, a16, None,
+                                    st) == want
+
+
 def test_size_limits_are_rejected_before_launch():
     """The decode attention addresses a sequence's containers with 32-bit
     offsets and puts sequences on the grid's y axis: past those limits it

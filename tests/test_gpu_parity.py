@@ -165,6 +165,35 @@ def test_other_key_mean_windows(window, tokens):
     run_case(None, 0, [0, 1], None, w=w, window=window)
 
 
+@pytest.mark.parametrize("hkv,d,cont", [(2, 32, (24, 18)), (4, 64, (80, 56)), (2, 256, (160, 112))])
+def test_encode_other_head_dims(hkv, d, cont):
+    """The write side at head dimensions other than 128 (the plan takes powers of
+    two from 32 to 256): containers, metadata, key means, drift counters and
+    decoded symbols bit-exact.  The decode attention is built for d = 128 and
+    reports KVQ_EUNSUPPORTED for these plans without launching anything."""
+    kvq = _kvq()
+    say(f"case head_dim={d} kv_heads={hkv} C={cont}")
+    w = synth.Workload(f"dim{d}", hkv, hkv, d, 2, 1, 256, 61 + d, "keymeans", (cont,), (0.0,))
+    plan = kvq.Plan(hkv, d, 8, 6, cont[0], cont[1], 128, 1.4)
+    p = O.OracleParams(hkv, d, 8, 6, cont[0], cont[1], 128, 1.4)
+    k, v = synth.cache_inputs(w, "cuda", [0, 1], None)
+    c, stats = gpu_encode(kvq, plan, k, v)
+    refs = [encode_cache_parallel(k[s].float().cpu().numpy(), v[s].float().cpu().numpy(), p) for s in range(2)]
+    compare_cache(c, stats, refs, p, 2)
+    for side, key, sk in ((0, "k_cont", "k_sym"), (1, "v_cont", "v_sym")):
+        sym = torch.empty(*c[key].shape[:2], p.n, dtype=torch.uint8, device="cuda")
+        ok = torch.zeros(*c[key].shape[:2], dtype=torch.int32, device="cuda")
+        kvq.kvq_decode_symbols(plan, side, c[key], sym, ok)
+        torch.cuda.synchronize()
+        assert int(ok.sum()) == ok.numel()
+        for s in range(2):
+            assert np.array_equal(sym[s].cpu().numpy(), refs[s][sk])
+    q = synth.queries(w, "cuda", [0, 1])
+    with pytest.raises(kvq.KvqError) as e:
+        gpu_attention(kvq, plan, q, c, hkv)
+    assert e.value.status == -3
+
+
 def test_encode_is_deterministic():
     kvq = _kvq()
     w = synth.WORKLOADS["heavy"]
