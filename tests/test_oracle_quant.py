@@ -185,3 +185,145 @@ def test_refit_exact_recovery_flat_and_guard():
     x = -np.arange(8, dtype=np.float32)[None, :]
     s1, o1 = O.refit_f64(x, m, np.array([0.125], np.float32), np.array([-7.0], np.float32))
     assert s1[0] == 0.125 and o1[0] == -7.0
+
+
+# ---------------------------------------------------------------------------
+# The drift bracket anchor ([D-Quant] Appendix A, Algorithm 1: the bisection on
+# log2 lambda runs between hi = log2(8 (max D - min D)) and hi - 40).  The
+# reading fixes hi to the exact ceiling of log2(8 Delta), Delta = RN(max D -
+# min D) over the float32 distortion matrix.  These pins recompute Delta and
+# the ceiling in exact rational arithmetic, without numpy float32 operations
+# or frexp, so an anchor one octave off (a floor, or the frexp exponent taken
+# as is) fails them.
+
+from fractions import Fraction
+
+
+def _rn32(q):
+    """Round a rational to the nearest binary32 value (ties to even, with
+    subnormals), returned as an exact Fraction."""
+    q = Fraction(q)
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
+    ulp = Fraction(2) ** (max(e, -126) - 23)
+    m, r = divmod(a, ulp)
+    m = int(m)
+    if r > ulp / 2 or (r == ulp / 2 and m % 2 == 1):
+        m += 1
+    assert m * ulp < Fraction(2) ** 128, "overflows binary32"
+    return sign * m * ulp
+
+
+def _f32_exact(v):
+    return Fraction(float(np.float32(v)))
+
+
+def _exact_anchor(x_row, s, o, vals):
+    """hi0 = min{h : 2^h >= 8 Delta} with Delta = RN32(max D - min D) and
+    D_im = RN32(RN32(x_i - RN32(o + RN32(s v_m)))^2), all in exact rationals.
+    Returns None when 8 Delta == 0."""
+    s, o = _f32_exact(s), _f32_exact(o)
+    rec = [_rn32(o + _rn32(s * Fraction(float(v)))) for v in vals]
+    D = []
+    for xi in x_row:
+        xi = _f32_exact(xi)
+        for r in rec:
+            dl = _rn32(xi - r)
+            D.append(_rn32(dl * dl))
+    y = 8 * _rn32(max(D) - min(D))
+    if y == 0:
+        return None
+    h = y.numerator.bit_length() - y.denominator.bit_length() - 1
+    while Fraction(2) ** h < y:
+        h += 1
+    while Fraction(2) ** (h - 1) >= y:
+        h -= 1
+    return h
+
+
+@pytest.mark.parametrize("scale", [1.0, 3.0e-3, 7.0e5, 2.0 ** -70])
+def test_drift_bracket_anchor_is_exact_ceiling(scale):
+    """The first bisection midpoint is (lo + hi) / 2 = 512 hi0 - 10240 on the
+    1/512-octave grid, for hi0 recomputed exactly.  The scales include one
+    whose distortions are binary32 subnormals (2^-70 squared is below 2^-126)."""
+    rng = np.random.default_rng(31)
+    M = 4
+    n = 6
+    x = (rng.standard_normal((5, n)) * scale).astype(np.float32)
+    s, o = O.fit_minmax(x, M)
+    r = _rates(O.integer_table(O.sharpen(np.array([0.1, 0.4, 0.4, 0.1]), 1.0)))
+    tr = []
+    O.drift(x, s, o, r, budget_fx(2), O.lambda_table(), trace=tr)
+    for i in range(x.shape[0]):
+        hi0 = _exact_anchor(x[i], s[i], o[i], range(M))
+        assert hi0 is not None
+        assert int(tr[0][i]) == 512 * hi0 - 10240, (i, hi0, int(tr[0][i]))
+    if scale == 2.0 ** -70:
+        assert hi0 < -100
+
+
+def test_drift_bracket_anchor_at_exact_power_of_two():
+    """8 Delta = 8 exactly (x = 0 and 1 on the grid {0, 1}): hi0 = 3, not the
+    frexp exponent 4 of 8 = 0.5 * 2^4; and 8 Delta = 18 gives hi0 = 5."""
+    r = np.array([65536 + 8192, 65536])
+    E = O.lambda_table()
+    for xs, hi0 in (([0.0, 1.0], 3), ([0.0, 1.5], 5)):
+        x = np.array([xs], np.float32)
+        assert _exact_anchor(x[0], 1.0, 0.0, range(2)) == hi0
+        tr = []
+        O.drift(x, np.array([1.0], np.float32), np.array([0.0], np.float32), r, budget_fx(2), E, trace=tr)
+        assert int(tr[0][0]) == 512 * hi0 - 10240
+
+
+def test_drift_top_of_bracket_takes_the_cheapest_level():
+    """The page's bracket top: at lambda = 2^hi >= 8 (max D - min D), any level
+    whose rate exceeds the cheapest one's by more than 1/8 bit costs more than
+    any distortion it saves, so the assignment at 2^hi is all-cheapest and
+    fits the smallest budget without the fallback.  Here 8 Delta = 40 (D = 9
+    and 4 for x = 3 on the grid {0, 1}), so the ceiling gives lambda = 64; a
+    floor would give 32, where level 0 still wins (-5 + 32 (1/8 + 2^-16) < 0)
+    and the encoder would fall back."""
+    E = O.lambda_table()
+    r = np.array([65536 + 8192 + 1, 65536])         # 1/8 bit + 2^-16 more for level 0
+    x = np.full((1, 4), 3.0, np.float32)
+    s = np.array([1.0], np.float32)
+    o = np.array([0.0], np.float32)
+    assert _exact_anchor(x[0], s[0], o[0], range(2)) == 6
+    tr = []
+    m, fb = O.drift(x, s, o, r, 4 * 65536, E, trace=tr)
+    assert not fb[0]
+    assert np.all(m == 1)
+    assert int(tr[0][0]) == 512 * 6 - 10240
+
+
+def test_drift_bottom_of_bracket_is_nearest_rounding():
+    """At lambda = 2^(hi0 - 40) the rate term is at most 2^-37 Delta times the
+    largest rate in bits, so the Lagrangian argmin is nearest-level rounding
+    except where two levels' distortions are that close (near-ties)."""
+    from oracle.quant import _assign, _distortion
+    rng = np.random.default_rng(32)
+    E = O.lambda_table()
+    for M, C in ((8, 331), (6, 231)):
+        f, c = O.build_table(M, 1024, 1.4)
+        r = _rates(f)
+        x = rng.standard_normal((8, 1024)).astype(np.float32)
+        s, o = O.fit_minmax(x, M)
+        D = _distortion(x, s, o, M)
+        rate_f32 = (r.astype(np.float64) / 65536).astype(np.float32)
+        # the first midpoint is hi0 - 20 octaves (pinned exactly above); lo is 20 below it
+        tr = []
+        O.drift(x, s, o, r, budget_fx(C), E, trace=tr)
+        lo_u = np.asarray(tr[0], np.int64) - 10240
+        m, _ = _assign(D, rate_f32, r, lo_u, E)
+        near = O.nearest_levels(x, s, o, M)
+        diff = np.nonzero(m != near)
+        lam = np.ldexp(2.0, lo_u // 512)           # >= lambda(lo_u)
+        for i, j in zip(*diff):
+            gap = abs(float(D[i, j, m[i, j]]) - float(D[i, j, near[i, j]]))
+            assert gap <= lam[i] * float(rate_f32.max()) + 4 * float(np.spacing(D[i, j].max())), (i, j)
