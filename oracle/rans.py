@@ -1,11 +1,11 @@
 """rANS coder and the fixed-size container.
 
-Follows [D-Quant] §3.1 Eq. (2) (Enc / Dec of the integer state with precision
-p = 8; symbols are encoded backwards so that decoding runs forwards), §4.2
-Eq. (3) (a stream occupies exactly C bytes; sigma is the final-state
-overhead) and Appendix A, Algorithm 2 (the state is read little-endian from
-the first sigma/8 bytes; each step looks up T[z] for z = x mod 2^p, updates
-x = f floor(x / 2^p) + z - c, then shifts in one byte at a time while x < L).
+Follows [D-Quant] §3.1 Eq. (2) (the encoder maps state x and symbol m to
+floor(x / f_m) 2^p + (x mod f_m) + c_m with precision p = 8; symbols are
+encoded backwards so that decoding yields them in stream order), §4.2 Eq. (3)
+(a stream occupies exactly C bytes, sigma bits of which hold the final state)
+and Appendix A, Algorithm 2 (which states that the decoder starts from the
+little-endian state at the head of the container and consumes bytes forwards).
 
 Readings (the page leaves them open):
   * 32-bit state, L = 2^23, sigma = 32, so the state lives in [2^23, 2^31).
@@ -14,11 +14,15 @@ Readings (the page leaves them open):
   * Container: bytes 0..3 hold the final state little-endian, then the pushed
     bytes in reverse push order (the last pushed byte is read first), then
     zero bytes up to C.
+
+The decoder here is written as the inverse of that encoder: each symbol is
+recovered by undoing Eq. (2), and each byte the encoder pushed to keep its
+state below 2^23 f_m is pulled back when the state drops below L.
 """
 
 import numpy as np
 
-from .model import L_RANS, PROB_BITS, decode_table
+from .model import L_RANS, PROB_BITS
 
 _U64 = np.uint64
 
@@ -61,14 +65,33 @@ def rans_encode(m, f, c, container_bytes):
     return cont, k
 
 
-def rans_decode(cont, f, c, n):
-    """Decode n symbols from each container row (Algorithm 2).
+def _undo_eq2(xp, f, c):
+    """Inverse of Eq. (2) for one state per row.
 
-    Returns (m [N, n] int64, end_state [N], bytes_read [N]).  Raises if a
-    stream would read past its container."""
+    The encoder's output x' = floor(x / f_m) 2^p + (x mod f_m) + c_m has its
+    low p bits, the slot x' mod 2^p = (x mod f_m) + c_m, inside
+    [c_m, c_m + f_m), and those intervals tile [0, 2^p) in symbol order; so m
+    is the last symbol whose cumulative frequency c_m does not exceed the slot,
+    and x = f_m floor(x' / 2^p) + (slot - c_m)."""
+    slot = xp & ((1 << PROB_BITS) - 1)
+    m = np.searchsorted(c, slot, side="right") - 1
+    return m, f[m] * (xp >> PROB_BITS) + (slot - c[m])
+
+
+def rans_decode(cont, f, c, n):
+    """Recover the n symbols of each container row by running the encoder
+    backwards: read the final state, undo Eq. (2) once per symbol in stream
+    order, and after each step pull back, one at a time, the bytes the encoder
+    pushed before that step (it pushed while its state was at least 2^23 f_m,
+    which leaves the undone state below L = 2^23 exactly when a byte is due).
+
+    Returns (m [N, n] int64, end_state [N], bytes_read [N]); a well-formed
+    stream ends at the encoder's start state L.  Raises if a stream would read
+    past its container."""
     cont = np.asarray(cont, np.uint8)
     N, C = cont.shape
-    sym, fz, bias = decode_table(f, c)
+    f = np.asarray(f, np.int64)
+    c = np.asarray(c, np.int64)
     x = np.zeros(N, np.int64)
     for b in range(4):
         x |= cont[:, b].astype(np.int64) << (8 * b)
@@ -76,14 +99,12 @@ def rans_decode(cont, f, c, n):
     out = np.zeros((N, n), np.int64)
     rows = np.arange(N)
     for i in range(n):
-        z = x & 255
-        out[:, i] = sym[z]
-        x = fz[z] * (x >> PROB_BITS) + bias[z]
+        out[:, i], x = _undo_eq2(x, f, c)
         while True:
-            ren = x < L_RANS
-            if not ren.any():
+            due = x < L_RANS
+            if not due.any():
                 break
-            r = rows[ren]
+            r = rows[due]
             if (ptr[r] >= C).any():
                 raise ValueError("decoder ran past the container")
             x[r] = (x[r] << 8) | cont[r, ptr[r]].astype(np.int64)

@@ -105,3 +105,22 @@ def test_budget_implies_fit():
     assert keep.sum() > 0
     cont, k = O.rans_encode(m[keep], f, c, C)
     assert np.all(4 + k <= C)
+
+
+@pytest.mark.parametrize("M,C", [(8, 331), (6, 231), (3, 200)])
+def test_decode_then_reencode_reproduces_the_container(M, C):
+    """The decoder inverts the encoder: encoding the decoded symbols again gives
+    the same C bytes, for random symbol streams drawn from the table itself."""
+    rng = np.random.default_rng(M + C)
+    f, c = O.build_table(M, 1024, 1.4)
+    q = np.asarray(f, np.float64) / 256.0
+    m = rng.choice(M, size=(32, 1024), p=q)
+    r = O.rate_table(f)
+    fits = r[m].sum(axis=1) <= O.budget_fx(C)
+    m = m[fits]
+    cont, _ = O.rans_encode(m, f, c, C)
+    sym, x_end, ptr = O.rans_decode(cont, f, c, 1024)
+    assert np.array_equal(sym, m)
+    assert np.all(x_end == O.L_RANS)
+    again, _ = O.rans_encode(sym, f, c, C)
+    assert np.array_equal(again, cont)
