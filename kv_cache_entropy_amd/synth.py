@@ -107,8 +107,23 @@ def sequence_kv(w, s, device, tokens=None):
             v = torch.randn(T, n, generator=g, device=device)
         elif w.dist == "heavy":
             def student_t4():
+                # t(4) = z0 / sqrt((z1^2 + ... + z4^2) / 4), every step one
+                # correctly rounded IEEE operation, so that the CPU generator
+                # gives the same bits on every host (a library reduction may
+                # group the terms differently, a vectorised sqrt may round
+                # differently)
                 z = torch.randn(5, T, n, generator=g, device=device)
-                return z[0] / torch.sqrt((z[1:] ** 2).sum(0) / 4.0)
+                ss = z[1] * z[1]
+                for i in (2, 3, 4):
+                    ss = ss + z[i] * z[i]
+                ss = ss / 4.0
+                if ss.device.type == "cpu":
+                    # the hardware square root (correctly rounded on every x86
+                    # host); a library's vectorised sqrt need not be
+                    den = torch.from_numpy(np.sqrt(ss.numpy()))
+                else:
+                    den = torch.sqrt(ss)
+                return z[0] / den
             k = student_t4()
             v = student_t4()
             ch = spike_channels(w, device)
