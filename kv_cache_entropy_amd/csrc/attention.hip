@@ -182,6 +182,47 @@ __device__ inline float wave_max_dpp(float v) {
   return __int_as_float(float_key(__builtin_amdgcn_readfirstlane(swap_rows_max_i(k))));
 }
 
+// Reduce-scatter of N per-lane values (N a power of two, at most 16) over the
+// wave: each halving stage pairs lanes that differ in one bit of the lane
+// index (quad xor 1 and 2, then row rotations by 4 and 8, which flip bit 2 and
+// bit 3 of a row position); a lane keeps the half of its values selected by
+// that bit and adds the partner's copy of the same half.  After log2 N stages
+// a lane holds one value; the remaining row stages and the two row swaps sum
+// it over the wave.  Lane l ends with the wave total of value
+// sum_k bit_k(l) * (N >> (k + 1)), k < log2 N.
+template <int N>
+__device__ inline float wave_sum_scatter(float (&v)[N], int lane) {
+  static_assert(N >= 1 && N <= 16 && (N & (N - 1)) == 0, "N must be a power of two up to 16");
+  int c = N;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bool hi = ((lane >> k) & 1) != 0;
+    if (c > 1) {
+      const int h = c / 2;
+#pragma unroll
+      for (int j = 0; j < N / 2; ++j) {
+        if (j < h) {
+          // the empty asm keeps the two selects as selects of values (not one
+          // dynamically indexed read of v)
+          float lo_v = v[j], hi_v = v[j + h];
+          asm("" : "+v"(lo_v), "+v"(hi_v));
+          const float keep = hi ? hi_v : lo_v;
+          const float send = hi ? lo_v : hi_v;
+          const float got = k == 0 ? dpp_f<0xB1>(send) : k == 1 ? dpp_f<0x4E>(send)
+                                                         : k == 2 ? dpp_f<0x124>(send) : dpp_f<0x128>(send);
+          v[j] = keep + got;
+        }
+      }
+      c = h;
+    } else {
+      const float got = k == 0 ? dpp_f<0xB1>(v[0]) : k == 1 ? dpp_f<0x4E>(v[0])
+                                                   : k == 2 ? dpp_f<0x124>(v[0]) : dpp_f<0x128>(v[0]);
+      v[0] += got;
+    }
+  }
+  return swap_rows_sum(v[0]);
+}
+
 // ------------------------------------------------------------------ prologue
 // One wave per (sequence, KV head, query slot v, chunk of 64 key-mean
 // windows): slot v < G is query head g G + v; slots up to the next multiple
@@ -727,6 +768,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   }
   for (int i = lane; i < 2 * NW * 64; i += 64) wts[i] = 0;
 
+  // lane l < 2G feeds the running sum of value sum_k bit_k(l) (2G >> (k + 1)):
+  // query head (that value) / 2, sum of p (even) or of p o (odd)
+  float* sum_slot = runL;
+  {
+    int idx = 0;
+#pragma unroll
+    for (int b = 0, w2 = G; w2 >= 1; ++b, w2 >>= 1) idx += ((lane >> b) & 1) * w2;
+    sum_slot = ((idx & 1) ? runZ : runL) + (idx >> 1);
+  }
   const uint32_t toffK = opaque(Lay::TABK + uint32_t(lane % Lay::REPS) * 4u);
   const uint32_t toffV = opaque(Lay::TABV + uint32_t(lane % Lay::REPS) * 4u);
   Ring5 rk, rv;
@@ -803,10 +853,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
         svK = h2f(a.v_so[2 * row]);
         ovK = h2f(a.v_so[2 * row + 1]);
         const int64_t wdx = tK >> a.log2W;
+        // logits are kept in log2 units: tau log2(e) folds into the affine terms
+        const float tl = a.tau * 1.4426950408889634f;
         for (int h = lane; h < HQ; h += 64) {
-          affS[h] = qscale[h];
-          affQ[h] = qsum[h];
-          affM[h] = qmu[h * a.nW + wdx];
+          affS[h] = tl * qscale[h];
+          affQ[h] = tl * qsum[h];
+          affM[h] = tl * qmu[h * a.nW + wdx];
         }
         wave_lds_fence();
       }
@@ -896,25 +948,36 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
       // ---- K head g done: logits -> online softmax -> weights for the next iteration
       if (kreal) {
         uint16_t* const wk = wts;
+        // Lazy running maximum: while no lane's logit exceeds a head's running
+        // maximum M, the weights are taken against M as it stands (exp2 of a
+        // non-positive number, so every weight stays in (0, 1]) and nothing is
+        // rescaled; only when some logit exceeds M is the tile maximum reduced,
+        // M raised and the head's sums and accumulators rescaled.  The tile's
+        // sums of p and p o over the wave, for all G heads at once, come from
+        // one reduce-scatter, and lane 2v + z (z = 0: sum p, 1: sum p o) adds
+        // its total to the running sum of head v.
+        float sums[2 * G];
 #pragma unroll
         for (int v = 0; v < NW; ++v) {
           const int m = v / 4, ii = v % 4;
           float whi = 0.f, wlo = 0.f;
           if (v < G) {
             const int h = g * G + v;
-            const float lg = a.tau * (sk * (D[m][ii] * affS[h]) + ok * affQ[h] + affM[h]);
-            const float tmax = wave_max_dpp(lg);
-            const float Mo = runM[h], Lo = runL[h], Zo = runZ[h];
-            const float Mn = fmaxf(Mo, tmax);
-            const float al = __expf(Mo - Mn);
-            const float p = __expf(lg - Mn);
-            const float ls = wave_sum_dpp(p);
-            const float zs = wave_sum_dpp(p * ovK);
-            runM[h] = Mn;
-            runL[h] = Lo * al + ls;
-            runZ[h] = Zo * al + zs;
+            const float lg = __builtin_fmaf(sk, D[m][ii] * affS[h], __builtin_fmaf(ok, affQ[h], affM[h]));
+            float Mr = runM[h];
+            if (__builtin_amdgcn_ballot_w64(lg > Mr) != 0) {
+              const float Mn = fmaxf(Mr, wave_max_dpp(lg));
+              const float al = __builtin_amdgcn_exp2f(Mr - Mn);
+              runL[h] *= al;
+              runZ[h] *= al;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) O[KJ][c][m][ii] *= al;
+              for (int c = 0; c < 2; ++c) O[KJ][c][m][ii] *= al;
+              Mr = Mn;
+              runM[h] = Mn;
+            }
+            const float p = __builtin_amdgcn_exp2f(lg - Mr);
+            sums[2 * v] = p;
+            sums[2 * v + 1] = p * ovK;
             const float wt = p * svK;
             const __half hh = __float2half_rn(wt);
             whi = wt;
@@ -923,6 +986,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
           wk[v * 64 + lane] = __half_as_ushort(__float2half_rn(whi));
           wk[NW * 64 + v * 64 + lane] = __half_as_ushort(__float2half_rn(wlo));
         }
+        const float tot = wave_sum_scatter<2 * G>(sums, lane);
+        if (lane < 2 * G) atomicAdd(sum_slot + g * G, tot);
         wave_lds_fence();
       }
       // rotate: the next step's V head (this step's K head) becomes O[0]
@@ -954,7 +1019,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
 #pragma unroll
           for (int c = 0; c < 2; ++c) P[h * (kD + 4) + c * 64 + lane] = O[g][c][m][ii];
           if (lane == 0) {
-            P[h * (kD + 4) + kD] = runM[h];
+            P[h * (kD + 4) + kD] = runM[h] * 0.6931471805599453f;      // back to natural log units
             P[h * (kD + 4) + kD + 1] = runL[h];
             P[h * (kD + 4) + kD + 2] = runZ[h];
           }
