@@ -190,6 +190,29 @@ kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q
                                 void* workspace, size_t workspace_bytes,
                                 void* hip_stream);
 
+/* kvq_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, whose role is taken
+ * by a library-owned scratch array of KVQ_NOALLOC_SCRATCH_BYTES per GPU (a
+ * static device array, held by every GPU the library runs on until the process
+ * ends; its address is looked up once per device on the first call there).
+ * The call allocates nothing and its kernels are those of kvq_decode_attention,
+ * so results are identical.  Returns KVQ_EWORKSPACE, launching nothing, when
+ * kvq_workspace_bytes(plan, 1, n_seqs, seq_len, n_q_heads) exceeds
+ * KVQ_NOALLOC_SCRATCH_BYTES (72 MiB covers, for example, 512 sequences of 8192
+ * tokens at 32/8 heads, or one of 131072 tokens at 64/8 heads), and KVQ_EDEVICE
+ * if the array's address cannot be obtained.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialised by the caller.  Nothing needs clearing between calls
+ * (every byte read was written earlier in the same call). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (72ull << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                                        const uint8_t* k_cont, const uint8_t* v_cont,
+                                        const uint16_t* k_so, const uint16_t* v_so,
+                                        const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                                        int64_t n_seqs, int64_t seq_len, float softmax_scale,
+                                        void* out, float* out_f32, void* hip_stream);
+
 /* Decode attention over a compressed prefix and an uncompressed bf16 tail
  * ([D-Quant] §5.1 "Implementation details": the most recent tokens are kept in
  * BF16; both parts join one softmax).  The query attends over

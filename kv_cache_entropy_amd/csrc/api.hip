@@ -1,6 +1,7 @@
 // C ABI entry points that launch device work (the host-only entry points are
 // in plan.cpp).  Argument checking happens here, before anything is enqueued.
 
+#include <mutex>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -398,6 +399,30 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
   return KVQ_OK;
 }
 
+// Scratch of kvq_decode_attention_noalloc: one array per GPU the library runs
+// on, held until the process ends.  In host code `noalloc_scratch_arr` only
+// names the symbol; its device address, one per device, comes from
+// hipGetSymbolAddress with that device current, on the entry point's first
+// call there, and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(KVQ_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) uint8_t noalloc_scratch_arr[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+bool noalloc_scratch(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch_arr)) != hipSuccess || !p) return false;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,6 +457,24 @@ kvq_status kvq_decode_attention(const kvq_plan* plan, const void* q, int32_t n_q
   return attention_impl(plan, q, n_q_heads, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, n_seqs,
                         seq_len, seq_len, nullptr, nullptr, 0, 0, softmax_scale, out, out_f32, workspace,
                         workspace_bytes, hip_stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_plan* plan, const void* q, int32_t n_q_heads,
+                                        const uint8_t* k_cont, const uint8_t* v_cont,
+                                        const uint16_t* k_so, const uint16_t* v_so,
+                                        const int8_t* k_mean_q, const uint16_t* k_mean_scale,
+                                        int64_t n_seqs, int64_t seq_len, float softmax_scale,
+                                        void* out, float* out_f32, void* hip_stream) {
+  if (!plan || seq_len < 1 || n_seqs < 1 || n_q_heads < 1) return KVQ_EINVAL;
+  size_t need = 0;
+  const kvq_status st = kvq_workspace_bytes(plan, 1, n_seqs, seq_len, n_q_heads, &need);
+  if (st != KVQ_OK) return st;
+  if (need > kNoAllocScratchBytes) return KVQ_EWORKSPACE;
+  void* ws = nullptr;
+  if (!noalloc_scratch(&ws)) return KVQ_EDEVICE;
+  return attention_impl(plan, q, n_q_heads, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, n_seqs,
+                        seq_len, seq_len, nullptr, nullptr, 0, 0, softmax_scale, out, out_f32, ws,
+                        kNoAllocScratchBytes, hip_stream);
 }
 
 kvq_status kvq_decode_attention_ex(const kvq_plan* plan, const void* q, int32_t n_q_heads,

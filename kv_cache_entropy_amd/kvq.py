@@ -53,6 +53,8 @@ _SIGS = {
                                     _P, _P, _P, ctypes.c_size_t, _P]),
     "kvq_encode_append": (_I32, [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P,
                                  _P, _P, _P]),
+    "kvq_decode_attention_noalloc": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64,
+                                            ctypes.c_float, _P, _P, _P]),
     "kvq_decode_attention_ex": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P,
                                        _I64, _I64, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "kvq_fixed_width_container_bytes": (_I32, [_I32, _I32, ctypes.POINTER(_I32)]),
@@ -233,6 +235,24 @@ def kvq_decode_attention(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_s
         plan.handle, _ptr(q, S * Hq * d * 2, "q"), Hq, *cp, S, T, float(softmax_scale),
         _ptr(out, S * Hq * d * 2, "out"), _ptr(out_f32, S * Hq * d * 4, "out_f32"),
         _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 72 << 20     # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def kvq_decode_attention_noalloc(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale, out,
+                                 out_f32=None, softmax_scale=0.0, stream=None):
+    """kvq_decode_attention without a workspace: the library's fixed scratch
+    array of NOALLOC_SCRATCH_BYTES per GPU takes its place."""
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("q and out must be bfloat16")
+    S, Hq = int(q.shape[0]), int(q.shape[1])
+    T = int(k_cont.shape[1])
+    d = plan.params.head_dim
+    cp = _cache_ptrs(plan, S, T, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scale)
+    _check("kvq_decode_attention_noalloc", lib().kvq_decode_attention_noalloc(
+        plan.handle, _ptr(q, S * Hq * d * 2, "q"), Hq, *cp, S, T, float(softmax_scale),
+        _ptr(out, S * Hq * d * 2, "out"), _ptr(out_f32, S * Hq * d * 4, "out_f32"), _stream(stream)))
 
 
 def kvq_encode_append(plan, k, v, cache, token_offset, stats=None, stream=None):

@@ -240,3 +240,20 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         kvq.Plan(2, 128)
     with pytest.raises(RuntimeError, match="missing"):
         kvq.kvq_model_probs(8, 1024)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_without_launching():
+    """kvq_decode_attention_noalloc checks the call's workspace size against its
+    fixed scratch array on the host and returns KVQ_EWORKSPACE before touching
+    any pointer or the device (so this runs without a GPU)."""
+    from kv_cache_entropy_amd import kvq
+    L = kvq.lib()
+    plan = kvq.Plan(8, 128, 8, 6, 331, 231, 128, 1.4)
+    a16 = ctypes.c_void_p(1 << 20)
+    S, T, Hq = 4096, 65536, 64
+    assert plan.workspace_bytes(1, S, T, Hq) > kvq.NOALLOC_SCRATCH_BYTES
+    st = L.kvq_decode_attention_noalloc(plan.handle, a16, Hq, a16, a16, a16, a16, a16, a16, S, T, 0.0,
+                                        a16, None, None)
+    assert st == -6
+    assert L.kvq_decode_attention_noalloc(None, a16, Hq, a16, a16, a16, a16, a16, a16, 1, 1024, 0.0,
+                                          a16, None, None) == -1
