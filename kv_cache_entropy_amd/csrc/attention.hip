@@ -554,6 +554,25 @@ struct Lay4 {
   static constexpr uint32_t SLOT_SHIFT = REPS == 16u ? 6u : 5u;     // log2(REPS * 4)
   static_assert(kWaves * SIZE <= 65536u, "per-wave regions must sit below 64 KiB");
   static_assert(TOTAL <= 163840u, "exceeds the LDS of a CU");
+
+  // Interleaved layout, used when it fits (PERM): decode-table slot z is row z
+  // (256 bytes) of a 64 KiB region at P_TAB - K replica r at byte 4 r, V
+  // replica r at byte 64 + 4 r - so the address of a lookup is one v_perm that
+  // puts the state's low byte in byte 1 of the lane's replica offset.  Bytes
+  // 128..255 of every row hold ring rows.  Rings then have a row pitch of 512
+  // bytes: lanes 0..31 in the upper half of one table row, lanes 32..63 in the
+  // next one (or, outside the table region, two rings share 512-byte rows,
+  // one at byte 0 and one at byte 128 of each half).  A lane keeps one bank.
+  static constexpr uint32_t P_TAB = (kWaves * SIZE + 255u) & ~255u;
+  static constexpr uint32_t P_RING_BYTES = 17u * 512u;
+  static constexpr int P_RINGS_IN_TAB = 7;                   // 7 x 17 of the 128 row pairs
+  static constexpr uint32_t P_RINGS = P_TAB + 65536u;
+  static constexpr int P_PAIRS = (2 * kWaves - P_RINGS_IN_TAB + 1) / 2;
+  static constexpr uint32_t P_TOTAL = P_RINGS + uint32_t(P_PAIRS) * P_RING_BYTES;
+  static constexpr bool PERM = P_TOTAL <= 163840u && P_TAB <= 65535u;
+  static constexpr uint32_t LDS_BYTES = PERM ? P_TOTAL : TOTAL;
+  static constexpr int RS = PERM ? 9 : 8;                    // log2 of the ring row pitch
+  static_assert(uint32_t(P_RINGS_IN_TAB) * P_RING_BYTES <= 65536u, "rings overflow the table region");
 };
 
 __device__ inline void wave_lds_fence() {
@@ -600,32 +619,38 @@ struct Ring5 {
   uint32_t ppos[2];     // their frame positions (kNoChunk: nothing to write)
 };
 
+template <int RS>
 __device__ inline uint32_t ring5_row(uint32_t pos, uint32_t off) {
-  // row (pos / 4) mod 16: one bit-field extract and one shift-add (opaque
-  // keeps the compiler from turning the extract into a shift and a mask)
-  return (opaque(__builtin_amdgcn_ubfe(pos, 2u, 4u)) << 8) + off;
+  // row (pos / 4) mod 16 at a pitch of 2^RS bytes: one bit-field extract and
+  // one shift-add (opaque keeps the compiler from turning the extract into a
+  // shift and a mask)
+  return (opaque(__builtin_amdgcn_ubfe(pos, 2u, 4u)) << RS) + off;
 }
 
 // Writes the 16-byte chunk at frame position pos (a multiple of 16, so its
 // four rows do not wrap), and row 16 with it when it lands on row 0.
+template <int RS>
 __device__ inline void ring5_write(uint8_t* lds, uint32_t off, uint32_t pos, const uint4& d) {
-  uint32_t* w = reinterpret_cast<uint32_t*>(lds + ring5_row(pos, off));
+  constexpr int R = 1 << (RS - 2);            // dwords per ring row
+  uint32_t* w = reinterpret_cast<uint32_t*>(lds + ring5_row<RS>(pos, off));
   w[0] = d.x;
-  w[64] = d.y;
-  w[128] = d.z;
-  w[192] = d.w;
-  if ((pos & 63u) == 0u) w[1024] = d.x;
+  w[R] = d.y;
+  w[2 * R] = d.z;
+  w[3 * R] = d.w;
+  if ((pos & 63u) == 0u) w[16 * R] = d.x;
 }
 
 // Bytes P .. P+3 of the stream (P's 8-byte window, shifted by P mod 4).
+template <int RS>
 __device__ inline uint32_t ring5_window(const Ring5& r, const uint8_t* lds) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(lds + ring5_row(r.P, r.off));
-  return __builtin_amdgcn_alignbyte(w[64], w[0], r.P);
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(lds + ring5_row<RS>(r.P, r.off));
+  return __builtin_amdgcn_alignbyte(w[1 << (RS - 2)], w[0], r.P);
 }
 
 // Starts a container (cont_off: its byte offset in the sequence's buffer
 // resource): fills the ring with the first 64 frame bytes (chunks past the
 // container are not fetched) and reads the 4-byte little-endian initial state.
+template <int RS>
 __device__ inline uint32_t ring5_start(Ring5& r, uint8_t* lds, __amdgpu_buffer_rsrc_t rs, uint32_t cont_off,
                                        uint32_t C) {
   const uint32_t off0 = cont_off & 15u;
@@ -635,11 +660,11 @@ __device__ inline uint32_t ring5_start(Ring5& r, uint8_t* lds, __amdgpu_buffer_r
 #pragma unroll
   for (int q = 0; q < 4; ++q) d[q] = load_chunk(rs, uint32_t(16 * q) < r.lim ? r.fo + 16u * q : kNoLoad);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ring5_write(lds, r.off, 16u * q, d[q]);
+  for (int q = 0; q < 4; ++q) ring5_write<RS>(lds, r.off, 16u * q, d[q]);
   r.F = 64u;
   r.ppos[0] = r.ppos[1] = kNoChunk;
   r.P = off0;
-  const uint32_t x = ring5_window(r, lds);
+  const uint32_t x = ring5_window<RS>(r, lds);
   r.P = off0 + 4u;
   return x;
 }
@@ -649,9 +674,9 @@ __device__ inline uint32_t ring5_start(Ring5& r, uint8_t* lds, __amdgpu_buffer_r
 // front.  Invariants (at most one byte per symbol): the bytes of the coming 16
 // symbols are written before they are read, and a chunk never overwrites
 // bytes not yet consumed.
-template <int S>
+template <int S, int RS>
 __device__ inline void ring5_block(Ring5& r, uint8_t* lds, __amdgpu_buffer_rsrc_t rs) {
-  if (r.ppos[S] != kNoChunk) ring5_write(lds, r.off, r.ppos[S], r.pend[S]);
+  if (r.ppos[S] != kNoChunk) ring5_write<RS>(lds, r.off, r.ppos[S], r.pend[S]);
   const bool real = (r.F < r.lim) && (r.F - r.P <= 48u);
   r.pend[S] = load_chunk(rs, real ? r.fo + r.F : kNoLoad);
   r.ppos[S] = real ? r.F : kNoChunk;
@@ -665,10 +690,17 @@ constexpr uint32_t kSel0 = 0x06050400u;
 // shifted in.  win holds the next 4 stream bytes and sel counts those already
 // taken in the current group of 4 symbols, so the update is branch-free and
 // reads no LDS besides the table.  Returns the table entry.
-template <uint32_t SLOT_SHIFT>
+// PERM: the table slot is row x mod 256 of the interleaved table region at
+// TAB, so the address is one v_perm: byte 0 from the lane's replica offset
+// toff, byte 1 the state's low byte, bytes 2..3 zero; TAB is an immediate.
+// Otherwise slot z holds its replicas contiguously (toff = table base + the
+// lane's replica offset) and the address is a shift and an and-or.
+template <bool PERM, uint32_t SLOT_SHIFT, uint32_t TAB>
 __device__ inline uint32_t dec5_step(uint32_t& x, uint32_t win, uint32_t& sel, const uint8_t* lds, uint32_t toff) {
   constexpr uint32_t mask = 0xFFu << SLOT_SHIFT;
-  const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + (((x << SLOT_SHIFT) & mask) | toff));
+  const uint32_t addr = PERM ? __builtin_amdgcn_perm(x, toff, 0x0C0C0400u) + TAB
+                             : (((x << SLOT_SHIFT) & mask) | toff);
+  const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + addr);
   const uint32_t m = opaque(__umul24(e & 0xFFu, x >> 8));
   x = m + ((e >> 8) & 0xFFu);
   const bool renorm = x < kStateLow;
@@ -728,20 +760,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
   constexpr int HQ = Lay::HQ;
   constexpr int NGM = (G + 3) / 4;
   constexpr int NW = Lay::NW;
-  __shared__ __align__(16) uint8_t lds[Lay::TOTAL];
+  constexpr bool PERM = Lay::PERM;
+  constexpr int RS = Lay::RS;
+  __shared__ __align__(16) uint8_t lds[Lay::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // decode tables, shared by the workgroup
-  for (int idx = tid; idx < 256 * int(Lay::REPS); idx += int(blockDim.x)) {
-    const uint32_t z = uint32_t(idx) / Lay::REPS;
+  // decode tables, shared by the workgroup (PERM: 16 replicas per table in
+  // each 256-byte row; otherwise REPS contiguous replicas per slot)
+  constexpr uint32_t NREP = PERM ? 16u : Lay::REPS;
+  for (int idx = tid; idx < 256 * int(NREP); idx += int(blockDim.x)) {
+    const uint32_t z = uint32_t(idx) / NREP;
     uint32_t mk = 0, mv = 0;
     for (int m = 1; m < a.Mk; ++m) mk = (z >= a.ck[m]) ? uint32_t(m) : mk;
     for (int m = 1; m < a.Mv; ++m) mv = (z >= a.cv[m]) ? uint32_t(m) : mv;
-    reinterpret_cast<uint32_t*>(lds + Lay::TABK)[idx] = a.fk[mk] | ((z - a.ck[mk]) << 8) | (a.lvk[mk] << 16);
-    reinterpret_cast<uint32_t*>(lds + Lay::TABV)[idx] = a.fv[mv] | ((z - a.cv[mv]) << 8) | (mv << 16);
+    const uint32_t ek = a.fk[mk] | ((z - a.ck[mk]) << 8) | (a.lvk[mk] << 16);
+    const uint32_t ev = a.fv[mv] | ((z - a.cv[mv]) << 8) | (mv << 16);
+    if (PERM) {
+      const uint32_t row = Lay::P_TAB + z * 256u + (uint32_t(idx) % NREP) * 4u;
+      *reinterpret_cast<uint32_t*>(lds + row) = ek;
+      *reinterpret_cast<uint32_t*>(lds + row + 64u) = ev;
+    } else {
+      reinterpret_cast<uint32_t*>(lds + Lay::TABK)[idx] = ek;
+      reinterpret_cast<uint32_t*>(lds + Lay::TABV)[idx] = ev;
+    }
   }
   __syncthreads();
 
@@ -777,11 +821,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
     for (int b = 0, w2 = G; w2 >= 1; ++b, w2 >>= 1) idx += ((lane >> b) & 1) * w2;
     sum_slot = ((idx & 1) ? runZ : runL) + (idx >> 1);
   }
-  const uint32_t toffK = opaque(Lay::TABK + uint32_t(lane % Lay::REPS) * 4u);
-  const uint32_t toffV = opaque(Lay::TABV + uint32_t(lane % Lay::REPS) * 4u);
+  uint32_t toffK, toffV;
   Ring5 rk, rv;
-  rk.off = opaque(Lay::RINGS + uint32_t(2 * w) * kRingBytes + uint32_t(lane) * 4u);
-  rv.off = opaque(Lay::RINGS + uint32_t(2 * w + 1) * kRingBytes + uint32_t(lane) * 4u);
+  if (PERM) {
+    toffK = opaque(uint32_t(lane % 16) * 4u);
+    toffV = opaque(64u + uint32_t(lane % 16) * 4u);
+    // ring i = 2 w + stream: the first P_RINGS_IN_TAB in the table rows' upper
+    // halves, the others in pairs after the table region
+    const uint32_t lane_off = uint32_t(lane >> 5) * 256u + uint32_t(lane & 31) * 4u;
+    auto ring_off = [&](int i) -> uint32_t {
+      if (i < Lay::P_RINGS_IN_TAB) return Lay::P_TAB + uint32_t(i) * Lay::P_RING_BYTES + 128u + lane_off;
+      const int j = i - Lay::P_RINGS_IN_TAB;
+      return Lay::P_RINGS + uint32_t(j / 2) * Lay::P_RING_BYTES + uint32_t(j % 2) * 128u + lane_off;
+    };
+    rk.off = opaque(ring_off(2 * w));
+    rv.off = opaque(ring_off(2 * w + 1));
+  } else {
+    toffK = opaque(Lay::TABK + uint32_t(lane % Lay::REPS) * 4u);
+    toffV = opaque(Lay::TABV + uint32_t(lane % Lay::REPS) * 4u);
+    rk.off = opaque(Lay::RINGS + uint32_t(2 * w) * kRingBytes + uint32_t(lane) * 4u);
+    rv.off = opaque(Lay::RINGS + uint32_t(2 * w + 1) * kRingBytes + uint32_t(lane) * 4u);
+  }
   wave_lds_fence();
 
   // fp16 high bytes of V levels 0..7 as a v_perm lookup (low byte is zero)
@@ -847,7 +907,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
       // ---- stream starts
       if (g == 0) {
         const int64_t row = s * a.T_cap + tK + lane;
-        xk = ring5_start(rk, lds, rsK, misK + uint32_t(tK + lane) * uint32_t(a.CK), uint32_t(a.CK));
+        xk = ring5_start<RS>(rk, lds, rsK, misK + uint32_t(tK + lane) * uint32_t(a.CK), uint32_t(a.CK));
         sk = h2f(a.k_so[2 * row]);
         ok = h2f(a.k_so[2 * row + 1]);
         svK = h2f(a.v_so[2 * row]);
@@ -868,7 +928,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
         // dummy on tile 0, and the ring must point at valid memory)
         const int64_t vt = (g == 0) ? i - 1 : i;               // V's tile (-1: dummy on tile 0)
         const int64_t tV = tb + 64 * (vt < 0 ? 0 : (vt >= NT ? NT - 1 : vt));
-        xv = ring5_start(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
+        xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
       }
 
       float4_t D[NGM];
@@ -900,21 +960,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
           // in the same registers across the loop's back edge
           const int b4 = 2 * b2 + bh;
           if (bh == 1) {
-            ring5_block<1>(rk, lds, rsK);
-            ring5_block<1>(rv, lds, rsV);
+            ring5_block<1, RS>(rk, lds, rsK);
+            ring5_block<1, RS>(rv, lds, rsV);
           } else {
-            ring5_block<0>(rk, lds, rsK);
-            ring5_block<0>(rv, lds, rsV);
+            ring5_block<0, RS>(rk, lds, rsK);
+            ring5_block<0, RS>(rv, lds, rsV);
           }
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
             uint32_t e[4];
-            const uint32_t winK = ring5_window(rk, lds), winV = ring5_window(rv, lds);
+            const uint32_t winK = ring5_window<RS>(rk, lds), winV = ring5_window<RS>(rv, lds);
             uint32_t selk = kSel0, selv = kSel0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              e[r] = dec5_step<Lay::SLOT_SHIFT>(xk, winK, selk, lds, toffK);
-              const uint32_t ev = dec5_step<Lay::SLOT_SHIFT>(xv, winV, selv, lds, toffV);
+              e[r] = dec5_step<PERM, Lay::SLOT_SHIFT, Lay::P_TAB>(xk, winK, selk, lds, toffK);
+              const uint32_t ev = dec5_step<PERM, Lay::SLOT_SHIFT, Lay::P_TAB>(xv, winV, selv, lds, toffV);
               vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
             }
             rk.P += selk - kSel0;
