@@ -1087,6 +1087,428 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
       }
 }
 
+// -------------------------------- attention, K and V decode in separate waves
+// The same per-step work as attention4_kernel, split between the two waves of
+// a pair that share one split (token range of one sequence): the K wave
+// decodes the K stream of (tile, KV head) and contracts it with the query,
+// runs the online softmax and writes the head's weights; the V wave decodes
+// the V stream of the same (tile, head) one step later and contracts it with
+// those weights.  Each wave runs one decode chain, and a CU holds 16 waves
+// (8 pairs, 4 waves per SIMD): the SIMDs' schedulers interleave four
+// independent chains where attention4_kernel interleaves two chains in each
+// of two waves.
+//
+// Steps are (tile, head) in order; one workgroup barrier per step: the K wave
+// passes barrier s after writing step s's weights into buffer s mod 2, the V
+// wave passes it before reading them.  Buffer s mod 2 is written again only
+// after barrier s + 1, which the V wave reaches after its step s.  Every wave
+// of the workgroup passes the same number of barriers (tokens_per_split / 64
+// times HKV): a pair whose split is shorter, or that has no split at all,
+// passes the remaining ones without work.
+//
+// LDS map: per pair (VCH: [64 ch][68] int8 V levels; WTS: 2 buffers of
+// [hi/lo][NW][64] fp16 weights; ALV: 2 buffers of the step's rescale factors
+// and a grow flag; RUN: running max, sums and the tile's affine terms), then
+// the pairs' rings (K ring 2p, V ring 2p + 1, 17 rows of 64 dwords), then the
+// K and V decode tables with REPS replicas (16, 8 or 4, the most that fit).
+constexpr int kPairs = 8;
+
+template <int G, int HKV>
+struct Lay5 {
+  static constexpr int HQ = G * HKV;
+  static constexpr int NW = ((G + 3) / 4) * 4;
+  static constexpr uint32_t VCH = 0;
+  static constexpr uint32_t WTS = 64u * kChunk8Stride;
+  static constexpr uint32_t WTS_BUF = 2u * NW * 64u * 2u;
+  static constexpr uint32_t ALV = WTS + 2u * WTS_BUF;              // 2 x [16] f32 (NW factors, flag at 15)
+  static constexpr uint32_t RUN = ALV + 2u * 64u;                  // 6 x [HQ] f32
+  static constexpr uint32_t SIZE = (RUN + 6u * HQ * 4u + 15u) & ~15u;
+  static constexpr uint32_t RINGS = (kPairs * SIZE + 255u) & ~255u;
+  static constexpr uint32_t RING_END = RINGS + 2u * kPairs * kRingBytes;
+  static constexpr uint32_t tab_end(uint32_t reps) {
+    return ((RING_END + 1024u * reps - 1u) / (1024u * reps) * (1024u * reps)) + 2u * 1024u * reps;
+  }
+  static constexpr uint32_t REPS = tab_end(16) <= 163840u ? 16u : tab_end(8) <= 163840u ? 8u : 4u;
+  static constexpr uint32_t TAB_BYTES = 256u * REPS * 4u;
+  static constexpr uint32_t TABK = (RING_END + TAB_BYTES - 1u) / TAB_BYTES * TAB_BYTES;
+  static constexpr uint32_t TABV = TABK + TAB_BYTES;
+  static constexpr uint32_t TOTAL = TABV + TAB_BYTES;
+  static constexpr uint32_t SLOT_SHIFT = REPS == 16u ? 6u : REPS == 8u ? 5u : 4u;
+  static_assert(TOTAL <= 163840u, "exceeds the LDS of a CU");
+
+  // Interleaved layout (PERM), when it fits: decode-table slot z is row z
+  // (256 bytes) of a 64 KiB region at P_TAB - K replica r at byte 4 r, V
+  // replica r at 64 + 4 r (16 each) - so a lookup address is one v_perm;
+  // bytes 128..255 of the rows hold 7 rings (row pitch 512 bytes, lanes
+  // 0..31 and 32..63 in two consecutive table rows); the other 9 rings follow
+  // in 512-byte rows shared by two rings (one at bytes 0 and 256, one at 128
+  // and 384), and the free half of the last of them holds each pair's running
+  // max, sums and rescale factors, 128 bytes apiece (HQ <= 32).
+  static constexpr uint32_t P_AFF = WTS + 2u * WTS_BUF;       // per pair: VCH, WTS, affine terms
+  static constexpr uint32_t P_SIZE = (P_AFF + 3u * HQ * 4u + 15u) & ~15u;
+  static constexpr uint32_t P_TAB = (kPairs * P_SIZE + 255u) & ~255u;
+  static constexpr uint32_t P_RING_BYTES = 17u * 512u;
+  static constexpr int P_RINGS_IN_TAB = 7;
+  static constexpr uint32_t P_RINGS = P_TAB + 65536u;
+  static constexpr int P_PAIRS = (2 * kPairs - P_RINGS_IN_TAB + 1) / 2;
+  static constexpr uint32_t P_TOTAL = P_RINGS + uint32_t(P_PAIRS) * P_RING_BYTES;
+  // piece k (128 bytes) of the free half of the last ring block
+  static constexpr uint32_t piece(int k) {
+    return P_RINGS + uint32_t(P_PAIRS - 1) * P_RING_BYTES + uint32_t(k >> 1) * 512u + uint32_t(k & 1) * 256u + 128u;
+  }
+  static constexpr bool PERM = NW == 4 && HQ <= 32 && (2 * kPairs - P_RINGS_IN_TAB) % 2 == 1 &&
+                               4 * kPairs <= 34 && P_TOTAL <= 163840u && P_TAB <= 65535u;
+  static constexpr uint32_t LDS_BYTES = PERM ? P_TOTAL : TOTAL;
+  static constexpr int RS = PERM ? 9 : 8;
+};
+
+// s_barrier with only LDS traffic ordered around it: container loads in
+// flight stay in flight.
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int G, int HKV>
+__global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a, int64_t S) {
+  using Lay = Lay5<G, HKV>;
+  constexpr int HQ = Lay::HQ;
+  constexpr int NGM = (G + 3) / 4;
+  constexpr int NW = Lay::NW;
+  constexpr bool PERM = Lay::PERM;
+  constexpr int RS = Lay::RS;
+  constexpr uint32_t TAB = PERM ? Lay::P_TAB : 0u;
+  __shared__ __align__(16) uint8_t lds[Lay::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pw = w >> 1;              // pair within the workgroup
+  const bool kwave = (w & 1) == 0;
+
+  constexpr uint32_t NREP = PERM ? 16u : Lay::REPS;
+  for (int idx = tid; idx < 256 * int(NREP); idx += int(blockDim.x)) {
+    const uint32_t z = uint32_t(idx) / NREP;
+    uint32_t mk = 0, mv = 0;
+    for (int m = 1; m < a.Mk; ++m) mk = (z >= a.ck[m]) ? uint32_t(m) : mk;
+    for (int m = 1; m < a.Mv; ++m) mv = (z >= a.cv[m]) ? uint32_t(m) : mv;
+    const uint32_t ek = a.fk[mk] | ((z - a.ck[mk]) << 8) | (a.lvk[mk] << 16);
+    const uint32_t ev = a.fv[mv] | ((z - a.cv[mv]) << 8) | (mv << 16);
+    if (PERM) {
+      const uint32_t row = Lay::P_TAB + z * 256u + (uint32_t(idx) % NREP) * 4u;
+      *reinterpret_cast<uint32_t*>(lds + row) = ek;
+      *reinterpret_cast<uint32_t*>(lds + row + 64u) = ev;
+    } else {
+      reinterpret_cast<uint32_t*>(lds + Lay::TABK)[idx] = ek;
+      reinterpret_cast<uint32_t*>(lds + Lay::TABV)[idx] = ev;
+    }
+  }
+  __syncthreads();
+
+  // lane offset of ring i (2 pw + stream)
+  auto ring_off = [&](int i) -> uint32_t {
+    if (PERM) {
+      const uint32_t lane_off = uint32_t(lane >> 5) * 256u + uint32_t(lane & 31) * 4u;
+      if (i < Lay::P_RINGS_IN_TAB) return Lay::P_TAB + uint32_t(i) * Lay::P_RING_BYTES + 128u + lane_off;
+      const int j = i - Lay::P_RINGS_IN_TAB;
+      return Lay::P_RINGS + uint32_t(j / 2) * Lay::P_RING_BYTES + uint32_t(j % 2) * 128u + lane_off;
+    }
+    return Lay::RINGS + uint32_t(i) * kRingBytes + uint32_t(lane) * 4u;
+  };
+
+  const int64_t gp = int64_t(blockIdx.x) * (blockDim.x >> 7) + pw;
+  const int64_t nsteps_all = (a.tokens_per_split / 64) * HKV;
+  if (gp >= S * a.nsplit) {                // no split: only the workgroup's barriers
+    for (int64_t k = 0; k < nsteps_all; ++k) step_barrier();
+    return;
+  }
+  const int64_t s = gp / a.nsplit;
+  const int split = int(gp - s * a.nsplit);
+
+  uint8_t* const mine = lds + uint32_t(pw) * (PERM ? Lay::P_SIZE : Lay::SIZE);
+  uint8_t* const vch = mine + Lay::VCH;
+  uint16_t* const wts = reinterpret_cast<uint16_t*>(mine + Lay::WTS);
+  float* const alv = reinterpret_cast<float*>(PERM ? lds + Lay::piece(4 * pw + 3) : mine + Lay::ALV);
+  float* const runM = reinterpret_cast<float*>(PERM ? lds + Lay::piece(4 * pw) : mine + Lay::RUN);
+  float* const runL = PERM ? reinterpret_cast<float*>(lds + Lay::piece(4 * pw + 1)) : runM + HQ;
+  float* const runZ = PERM ? reinterpret_cast<float*>(lds + Lay::piece(4 * pw + 2)) : runL + HQ;
+  float* const affS = PERM ? reinterpret_cast<float*>(mine + Lay::P_AFF) : runZ + HQ;
+  float* const affQ = affS + HQ;
+  float* const affM = affQ + HQ;
+
+  const int64_t tb = int64_t(split) * a.tokens_per_split;
+  const int64_t te = tb + a.tokens_per_split < a.T ? tb + a.tokens_per_split : a.T;
+  const int64_t NT = (te - tb) / 64;
+  float* P = a.part + (s * a.part_splits + split) * int64_t(HQ) * (kD + 4);
+  const int qn = lane & 3;
+
+  if (kwave) {
+    // ------------------------------------------------------------ K wave
+    for (int h = lane; h < HQ; h += 64) {
+      runM[h] = -__builtin_inff();
+      runL[h] = 0.f;
+      runZ[h] = 0.f;
+    }
+    float* sum_slot = runL;
+    {
+      int idx = 0;
+#pragma unroll
+      for (int b = 0, w2 = G; w2 >= 1; ++b, w2 >>= 1) idx += ((lane >> b) & 1) * w2;
+      sum_slot = ((idx & 1) ? runZ : runL) + (idx >> 1);
+    }
+    const uint32_t toffK = opaque(PERM ? uint32_t(lane % 16) * 4u : Lay::TABK + uint32_t(lane % Lay::REPS) * 4u);
+    Ring5 rk;
+    rk.off = opaque(ring_off(2 * pw));
+    wave_lds_fence();
+
+    const uint4* qop = a.qop + s * (HKV * NGM * 32 * 4);
+    const float* qscale = a.qscale + s * HQ;
+    const float* qsum = a.qsum + s * HQ;
+    const float* qmu = a.qmu + s * HQ * a.nW;
+    const int qc0 = 16 * ((lane >> 2) >> 3) + ((lane >> 2) & 7);
+    constexpr bool kQPrefetch = NGM == 1;
+    uint4 qnx[NGM][2];
+#pragma unroll
+    for (int m = 0; m < NGM; ++m)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) qnx[m][t] = kQPrefetch ? qop[(m * 32 + qc0 + 8 * t) * 4 + qn] : uint4{};
+
+    const uint8_t* const kseq = a.k_cont + s * a.T_cap * a.CK;
+    const __amdgpu_buffer_rsrc_t rsK = seq_rsrc(kseq, uint32_t(a.T * a.CK));
+    const uint32_t misK = uint32_t(reinterpret_cast<uintptr_t>(kseq) & 15u);
+    uint32_t xk = 0;
+    float sk = 0.f, ok = 0.f, svK = 0.f, ovK = 0.f;
+    int buf = 0;
+
+    for (int64_t i = 0; i < NT; ++i) {
+      const int64_t tK = tb + 64 * i;
+#pragma unroll 1
+      for (int g = 0; g < HKV; ++g) {
+        if (g == 0) {
+          const int64_t row = s * a.T_cap + tK + lane;
+          xk = ring5_start<RS>(rk, lds, rsK, misK + uint32_t(tK + lane) * uint32_t(a.CK), uint32_t(a.CK));
+          sk = h2f(a.k_so[2 * row]);
+          ok = h2f(a.k_so[2 * row + 1]);
+          svK = h2f(a.v_so[2 * row]);
+          ovK = h2f(a.v_so[2 * row + 1]);
+          const int64_t wdx = tK >> a.log2W;
+          // logits are kept in log2 units: tau log2(e) folds into the affine terms
+          const float tl = a.tau * 1.4426950408889634f;
+          for (int h = lane; h < HQ; h += 64) {
+            affS[h] = tl * qscale[h];
+            affQ[h] = tl * qsum[h];
+            affM[h] = tl * qmu[h * a.nW + wdx];
+          }
+          wave_lds_fence();
+        }
+        float4_t D[NGM];
+#pragma unroll
+        for (int m = 0; m < NGM; ++m) D[m] = float4_t{0.f, 0.f, 0.f, 0.f};
+        uint4 qh[NGM][2];
+        {
+          const int gn = kQPrefetch ? (g + 1 < HKV ? g + 1 : 0) : g;
+          const uint4* qg = qop + gn * (NGM * 32 * 4) + qn;
+#pragma unroll
+          for (int m = 0; m < NGM; ++m)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              if (kQPrefetch) {
+                qh[m][t] = qnx[m][t];
+                qnx[m][t] = qg[(m * 32 + qc0 + 8 * t) * 4];
+              } else {
+                qh[m][t] = qg[(m * 32 + qc0 + 8 * t) * 4];
+              }
+            }
+        }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll 1
+          for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+            for (int bh = 0; bh < 2; ++bh) {
+              if (bh == 1) ring5_block<1, RS>(rk, lds, rsK);
+              else ring5_block<0, RS>(rk, lds, rsK);
+#pragma unroll
+              for (int cc = 0; cc < 4; ++cc) {
+                uint32_t e[4];
+                const uint32_t winK = ring5_window<RS>(rk, lds);
+                uint32_t selk = kSel0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) e[r] = dec5_step<PERM, Lay::SLOT_SHIFT, TAB>(xk, winK, selk, lds, toffK);
+                rk.P += selk - kSel0;
+                const half4_t B = as_half4(__builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
+                                           __builtin_amdgcn_perm(e[3], e[2], 0x07060302u));
+#pragma unroll
+                for (int m = 0; m < NGM; ++m) {
+                  D[m] = mfma_bcast_a(as_half4(qh[m][0].x, qh[m][0].y), B, D[m], 8 * ch + 4 * bh + cc);
+                  D[m] = mfma_bcast_a(as_half4(qh[m][0].z, qh[m][0].w), B, D[m], 8 * ch + 4 * bh + cc);
+                }
+              }
+              if (bh == 1) {
+#pragma unroll
+                for (int m = 0; m < NGM; ++m) {
+                  const uint4 t = qh[m][0];
+                  qh[m][0] = qh[m][1];
+                  qh[m][1] = t;
+                }
+              }
+            }
+        }
+        // logits -> online softmax (lazy running maximum) -> weights of this step
+        uint16_t* const wk = wts + buf * (Lay::WTS_BUF / 2);
+        float* const al = alv + buf * 16;
+        float sums[2 * G];
+        bool grew = false;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+          const int m = v / 4, ii = v % 4;
+          float whi = 0.f, wlo = 0.f, alh = 1.f;
+          if (v < G) {
+            const int h = g * G + v;
+            const float lg = __builtin_fmaf(sk, D[m][ii] * affS[h], __builtin_fmaf(ok, affQ[h], affM[h]));
+            float Mr = runM[h];
+            if (__builtin_amdgcn_ballot_w64(lg > Mr) != 0) {
+              const float Mn = fmaxf(Mr, wave_max_dpp(lg));
+              alh = __builtin_amdgcn_exp2f(Mr - Mn);
+              runL[h] *= alh;
+              runZ[h] *= alh;
+              grew = true;
+              Mr = Mn;
+              runM[h] = Mn;
+            }
+            const float p = __builtin_amdgcn_exp2f(lg - Mr);
+            sums[2 * v] = p;
+            sums[2 * v + 1] = p * ovK;
+            const float wt = p * svK;
+            const __half hh = __float2half_rn(wt);
+            whi = wt;
+            wlo = wt - __half2float(hh);
+          }
+          wk[v * 64 + lane] = __half_as_ushort(__float2half_rn(whi));
+          wk[NW * 64 + v * 64 + lane] = __half_as_ushort(__float2half_rn(wlo));
+          if (lane == 0) al[v] = alh;
+        }
+        if (lane == 0) al[15] = grew ? 1.f : 0.f;
+        const float tot = wave_sum_scatter<2 * G>(sums, lane);
+        if (lane < 2 * G) atomicAdd(sum_slot + g * G, tot);
+        buf ^= 1;
+        step_barrier();
+      }
+    }
+    for (int64_t k = NT * HKV; k < nsteps_all; ++k) step_barrier();
+    wave_lds_fence();
+#pragma unroll
+    for (int v = 0; v < G; ++v)
+      for (int g = 0; g < HKV; ++g) {
+        const int h = g * G + v;
+        if (lane == 0) {
+          P[h * (kD + 4) + kD] = runM[h] * 0.6931471805599453f;      // back to natural log units
+          P[h * (kD + 4) + kD + 1] = runL[h];
+          P[h * (kD + 4) + kD + 2] = runZ[h];
+        }
+      }
+    return;
+  }
+
+  // -------------------------------------------------------------- V wave
+  const uint32_t toffV = opaque(PERM ? 64u + uint32_t(lane % 16) * 4u : Lay::TABV + uint32_t(lane % Lay::REPS) * 4u);
+  Ring5 rv;
+  rv.off = opaque(ring_off(2 * pw + 1));
+  const uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
+  const uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
+  const uint32_t lutLo2 = a.lbv[0] | (a.lbv[1] << 8) | (a.lbv[2] << 16) | (a.lbv[3] << 24);
+  const uint32_t lutHi2 = a.lbv[4] | (a.lbv[5] << 8) | (a.lbv[6] << 16) | (a.lbv[7] << 24);
+  // Output accumulators, rotated once per step so that V's head is O[0].
+  float4_t O[HKV][2][NGM];
+#pragma unroll
+  for (int g = 0; g < HKV; ++g)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) O[g][c][m] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* const vseq = a.v_cont + s * a.T_cap * a.CV;
+  const __amdgpu_buffer_rsrc_t rsV = seq_rsrc(vseq, uint32_t(a.T * a.CV));
+  const uint32_t misV = uint32_t(reinterpret_cast<uintptr_t>(vseq) & 15u);
+  uint32_t xv = 0;
+  int buf = 0;
+  for (int64_t i = 0; i < NT; ++i) {
+    const int64_t tV = tb + 64 * i;
+#pragma unroll 1
+    for (int g = 0; g < HKV; ++g) {
+      step_barrier();                                   // the K wave's weights of (i, g)
+      if (g == 0) xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
+      const uint16_t* const wv = wts + buf * (Lay::WTS_BUF / 2);
+      const uint16_t* const wv_lo = wv + NW * 64;
+      const float* const al = alv + buf * 16;
+      if (al[15] != 0.f) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int m = 0; m < NGM; ++m)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) O[0][c][m][ii] *= al[m * 4 + ii];
+      }
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll 1
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+          for (int bh = 0; bh < 2; ++bh) {
+            const int b4 = 2 * b2 + bh;
+            if (bh == 1) ring5_block<1, RS>(rv, lds, rsV);
+            else ring5_block<0, RS>(rv, lds, rsV);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+              const uint32_t winV = ring5_window<RS>(rv, lds);
+              uint32_t selv = kSel0;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const uint32_t ev = dec5_step<PERM, Lay::SLOT_SHIFT, TAB>(xv, winV, selv, lds, toffV);
+                vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
+              }
+              rv.P += selv - kSel0;
+            }
+          }
+        wave_lds_fence();
+        if (a.v_lo_nonzero) {
+          pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[0][ch]);
+        } else {
+          pv_half<NGM, false>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, 0u, 0u, O[0][ch]);
+        }
+        wave_lds_fence();
+      }
+      buf ^= 1;
+      if (HKV > 1) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int m = 0; m < NGM; ++m) {
+            const float4_t t = O[0][c][m];
+#pragma unroll
+            for (int j = 0; j + 1 < HKV; ++j) O[j][c][m] = O[j + 1][c][m];
+            O[HKV - 1][c][m] = t;
+          }
+      }
+    }
+  }
+  for (int64_t k = NT * HKV; k < nsteps_all; ++k) step_barrier();
+  // NT HKV rotations: O[j] holds KV head j
+#pragma unroll
+  for (int g = 0; g < HKV; ++g)
+#pragma unroll
+    for (int m = 0; m < NGM; ++m)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int v = m * 4 + ii;
+        if (v < G) {
+          const int h = g * G + v;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) P[h * (kD + 4) + c * 64 + lane] = O[g][c][m][ii];
+        }
+      }
+}
+
 // ------------------------------------------------ fixed-width comparator
 // [D-Quant] Appendix B compares the entropy-coded container with fixed-width
 // symbols at the same preprocessing.  Symbol i = 4c + r of a stream sits in
@@ -1363,11 +1785,24 @@ bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int 
   return affine && levels_k <= 9 && levels_v <= 9;
 }
 
+constexpr bool kUseSplitWaves = true;
+
 template <int G, int HKV>
 static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stream) {
   // the interleaved kernel keeps V levels as int8 and maps them to fp16 with
   // an 8-entry lookup, so it serves V alphabets of up to 8 levels
-  if (a.Mv <= 8) {
+  constexpr bool kSplit = kUseSplitWaves && (G <= 4 || HKV <= 2);
+  if constexpr (kSplit) {
+    if (a.Mv <= 8) {
+      const int64_t pairs = S * a.nsplit;
+      constexpr int64_t kCUs = 256;
+      int64_t ppw = (pairs + kCUs - 1) / kCUs;
+      ppw = ppw < 1 ? 1 : (ppw > kPairs ? kPairs : ppw);
+      hipLaunchKernelGGL((attention5_kernel<G, HKV>), dim3(unsigned((pairs + ppw - 1) / ppw)),
+                         dim3(unsigned(128 * ppw)), 0, stream, a, S);
+      return hipGetLastError();
+    }
+  } else if (a.Mv <= 8) {
     const int64_t waves = S * a.nsplit;
     // One workgroup per CU at a time (its LDS is sized for kWaves waves): a
     // launch too small to give every CU kWaves waves uses fewer waves per
@@ -1377,9 +1812,9 @@ static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stre
     wpw = wpw < 1 ? 1 : (wpw > kWaves ? kWaves : wpw);
     hipLaunchKernelGGL((attention4_kernel<G, HKV>), dim3(unsigned((waves + wpw - 1) / wpw)),
                        dim3(unsigned(64 * wpw)), 0, stream, a, S);
+    return hipGetLastError();
   }
-  else
-    hipLaunchKernelGGL((attention2_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((attention2_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
