@@ -1170,6 +1170,26 @@ __device__ __forceinline__ void step_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// pv_half for integer V levels (every fp16 level has a zero low byte): one
+// v_perm looks up the 4 high bytes, two more place them over zero low bytes.
+template <int NGM>
+__device__ inline void pv_half_int(const uint8_t* vch, int lane, int qn, const uint16_t* wv, const uint16_t* wv_lo,
+                                   uint32_t lutHi, uint32_t lutLo, float4_t (&O)[NGM]) {
+#pragma unroll 2
+  for (int tq = 0; tq < 16; ++tq) {
+    const uint32_t idx = *reinterpret_cast<const uint32_t*>(vch + lane * kChunk8Stride + 4 * tq);
+    const uint32_t hb = __builtin_amdgcn_perm(lutHi, lutLo, idx);
+    const half4_t B = as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu), __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
+#pragma unroll
+    for (int m = 0; m < NGM; ++m) {
+      const uint2 ah = *reinterpret_cast<const uint2*>(wv + (m * 4 + qn) * 64 + 4 * tq);
+      const uint2 al = *reinterpret_cast<const uint2*>(wv_lo + (m * 4 + qn) * 64 + 4 * tq);
+      O[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah.x, ah.y), B, O[m], 0, 0, 0);
+      O[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[m], 0, 0, 0);
+    }
+  }
+}
+
 template <int G, int HKV>
 __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a, int64_t S) {
   using Lay = Lay5<G, HKV>;
@@ -1415,11 +1435,16 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   const uint32_t toffV = opaque(PERM ? 64u + uint32_t(lane % 16) * 4u : Lay::TABV + uint32_t(lane % Lay::REPS) * 4u);
   Ring5 rv;
   rv.off = opaque(ring_off(2 * pw + 1));
-  const uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
-  const uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
+  // fp16 bytes of the V levels as v_perm lookups, kept in VGPRs (the empty asm
+  // stops the compiler from rebuilding them from SGPRs in the PV loop)
+  uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
+  uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
   const uint32_t lutLo2 = a.lbv[0] | (a.lbv[1] << 8) | (a.lbv[2] << 16) | (a.lbv[3] << 24);
   const uint32_t lutHi2 = a.lbv[4] | (a.lbv[5] << 8) | (a.lbv[6] << 16) | (a.lbv[7] << 24);
-  // Output accumulators, rotated once per step so that V's head is O[0].
+  asm volatile("" : "+v"(lutLo), "+v"(lutHi));
+  const bool lo_levels = a.v_lo_nonzero != 0;
+  // Output accumulators, rotated once per step so that V's head is O[0]; after
+  // NT HKV steps O[j] holds KV head j again.
   float4_t O[HKV][2][NGM];
 #pragma unroll
   for (int g = 0; g < HKV; ++g)
@@ -1471,14 +1496,14 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
             }
           }
         wave_lds_fence();
-        if (a.v_lo_nonzero) {
+        if (lo_levels)
           pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[0][ch]);
-        } else {
-          pv_half<NGM, false>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, 0u, 0u, O[0][ch]);
-        }
+        else
+          pv_half_int<NGM>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, O[0][ch]);
         wave_lds_fence();
       }
       buf ^= 1;
+      // rotate: the next step's head becomes O[0]
       if (HKV > 1) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -1493,7 +1518,6 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
     }
   }
   for (int64_t k = NT * HKV; k < nsteps_all; ++k) step_barrier();
-  // NT HKV rotations: O[j] holds KV head j
 #pragma unroll
   for (int g = 0; g < HKV; ++g)
 #pragma unroll
