@@ -3,14 +3,19 @@
 on one MI355X, with the write side (encode) timed in the same run.
 
     python bench.py [--steps K] [--warmup W] [--workload gqa|long|verylong|heavy|tiny]
+                    [--budget B] [--no-configs] [--no-cpu-baseline]
 
 One decode step = one query token per sequence attending over the whole
 resident compressed cache of every layer (prologue, fused rANS-decode +
 attention kernel, split combine).  `value` is the algorithmic compressed bytes
 of one step (containers + fp16 scale/offset + INT8 key means and their
-scales) divided by the step time, in GB/s.  The cache is encoded once from
-seeded synthetic K/V first (kvq_encode_streams), and that encode is timed too.
-Prints one JSON line on stdout; progress goes to stderr.
+scales) divided by the step time, in GB/s, for the headline workload (gqa at
+2.26 bits/elem unless --workload/--budget say otherwise).  Every workload is
+encoded from seeded synthetic K/V on the GPU first (kvq_encode_streams), and
+that encode is timed too.  `configs` repeats the measurement for every other
+workload and budget (one record each), and `cpu_baseline` times the oracle's
+two legs on a bounded sample.  Prints one JSON line on stdout; progress goes
+to stderr.
 """
 
 import argparse
@@ -62,6 +67,294 @@ def measured_traffic(workload_key, bytes_hint):
     return rec.get("hbm_bytes_per_launch")
 
 
+def kernel_name(w, levels_v=6):
+    """The fused kernel the library launches for this head layout (its dispatch
+    rule: K and V in separate waves up to 4 query heads per KV head, or 8 on at
+    most 2 KV heads; otherwise one wave with both decode chains)."""
+    G = w.n_q_heads // w.n_kv_heads
+    if levels_v > 8:
+        return f"attention2_kernel<{G}, {w.n_kv_heads}>"
+    if G <= 4 or w.n_kv_heads <= 2:
+        return f"attention5_kernel<{G}, {w.n_kv_heads}>"
+    return f"attention4_kernel<{G}, {w.n_kv_heads}>"
+
+
+def run_config(torch, kvq, synth, w, bi, args, dev, extras=False, cpu_sample=False):
+    """Encodes one workload at one budget and times its decode steps.  Returns
+    (record, samples for the CPU baseline or None)."""
+    ck, cv = w.containers[bi]
+    S, T, n, Hq, d = w.n_seqs, w.seq_len, w.n, w.n_q_heads, w.head_dim
+    plan = kvq.Plan(w.n_kv_heads, d, 8, 6, ck, cv, 128, 1.4)
+    nW = T // 128
+    log(f"[bench] workload={w.name} S={S} T={T} Hq={Hq} Hkv={w.n_kv_heads} C=({ck},{cv})")
+
+    # ---- seeded inputs, resident in HBM
+    kdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    k = torch.empty(S, T, n, dtype=kdt, device=dev)
+    v = torch.empty(S, T, n, dtype=kdt, device=dev)
+    for s in range(S):
+        ks, vs = synth.sequence_kv(w, s, dev)
+        k[s].copy_(ks)
+        v[s].copy_(vs)
+    q = synth.queries(w, dev)
+    torch.cuda.synchronize()
+
+    # ---- write side
+    cache = kvq.alloc_cache(plan, S, T, dev)
+    stats = torch.zeros(8, dtype=torch.int64, device=dev)
+
+    def encode():
+        kvq.kvq_encode_streams(plan, k, v, cache["k_cont"], cache["v_cont"], cache["k_so"],
+                               cache["v_so"], cache["k_mean_q"], cache["k_mean_scale"], stats=stats)
+
+    encode()
+    torch.cuda.synchronize()
+    stats_once = stats.cpu().tolist()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.encode_reps):
+        encode()
+    e1.record()
+    torch.cuda.synchronize()
+    encode_ms = e0.elapsed_time(e1) / args.encode_reps
+    log(f"[bench]   encode {encode_ms:.2f} ms for {S * T} token-layers")
+    fw = None
+    if extras and w.n % 1024 == 0 and w.dtype == "bf16":
+        # the fixed-width comparator of the same cache ([D-Quant] Appendix B: same
+        # preprocessing, nearest rounding at 6/3 levels, power-of-two widths)
+        fk, fv = kvq.kvq_fixed_width_container_bytes(6, n), kvq.kvq_fixed_width_container_bytes(3, n)
+        plan_fw = kvq.Plan(w.n_kv_heads, d, 6, 3, fk, fv, 128, 1.4)
+        cache_fw = kvq.alloc_cache(plan_fw, S, T, dev)
+        kvq.kvq_encode_fixed_width(plan_fw, k, v, cache_fw["k_cont"], cache_fw["v_cont"], cache_fw["k_so"],
+                                   cache_fw["v_so"], cache_fw["k_mean_q"], cache_fw["k_mean_scale"])
+        torch.cuda.synchronize()
+        fw = (plan_fw, cache_fw, fk, fv)
+    samples = None
+    if cpu_sample:
+        base_seqs = [0, S - 1] if S > 1 else [0]
+        base_tokens = min(T, 512)
+        enc_tokens = T if S * T > 2 * 4096 else min(T, 4096)    # whole sequences where the sample allows
+        samples = {"seqs": base_seqs, "tokens": base_tokens, "enc_tokens": enc_tokens,
+                   "k": [k[s, :enc_tokens].float().cpu().numpy() for s in base_seqs],
+                   "v": [v[s, :enc_tokens].float().cpu().numpy() for s in base_seqs],
+                   "q": [q[s].float().cpu().numpy() for s in base_seqs]}
+    W = 128
+    stream_ok = extras and T >= 2 * W
+    if stream_ok:
+        win_k = k[:, T - W:].contiguous()
+        win_v = v[:, T - W:].contiguous()
+        win_k16 = win_k.to(torch.bfloat16)
+        win_v16 = win_v.to(torch.bfloat16)
+    del k, v
+    torch.cuda.empty_cache()
+
+    # ---- read side: rotate copies when the working set would sit in cache
+    step_bytes = S * T * (ck + cv + 8) + S * nW * (n + 2)
+    kernel_bytes = S * T * (ck + cv + 8)
+    copies = max(1, math.ceil((1 << 30) / step_bytes))
+    if copies > 1:
+        # one flat buffer per field, each copy at a 256-byte aligned stride
+        # (the library requires 16-byte aligned base pointers)
+        caches = [dict() for _ in range(copies)]
+        for key, t in cache.items():
+            nb = t.numel() * t.element_size()
+            stride = (nb + 255) // 256 * 256
+            flat = torch.empty(copies * stride, dtype=torch.uint8, device=dev)
+            src = t.contiguous().view(torch.uint8).reshape(-1)
+            for i in range(copies):
+                part = flat[i * stride:i * stride + nb]
+                part.copy_(src)
+                caches[i][key] = part.view(t.dtype).view(t.shape)
+    else:
+        caches = [cache]
+    ws = torch.empty(plan.workspace_bytes(1, S, T, Hq), dtype=torch.uint8, device=dev)
+    out = torch.empty(S, Hq, d, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        c = caches[i % copies]
+        kvq.kvq_decode_attention(plan, q, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
+                                 c["k_mean_q"], c["k_mean_scale"], out, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kvq.kvq_timing_collect()
+    kvq.kvq_timing_enable(True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    kvq.kvq_timing_enable(False)
+    ms = t0.elapsed_time(t1) / args.steps
+    kms, klaunch = kvq.kvq_timing_collect()
+    kernel_ms = kms / max(1, klaunch)
+    symbols = S * T * 2 * n
+    kgbs = kernel_bytes / (kernel_ms * 1e-3) / 1e9
+    alu = symbols * DECODE_OPS_PER_SYMBOL / (kernel_ms * 1e-3) / 1e12
+    log(f"[bench]   step {ms:.4f} ms ({step_bytes / (ms * 1e-3) / 1e9:.1f} GB/s); attention kernel "
+        f"{kernel_ms:.4f} ms ({kgbs:.1f} GB/s, {kgbs / HBM_PEAK_GBS:.4f} of HBM peak) over {klaunch} launches")
+    rec = {
+        "workload": w.name, "budget_bits_per_elem": w.budgets[bi], "containers": [ck, cv], "levels": [8, 6],
+        "shape": {"n_seqs": S, "batch": w.batch, "layers": w.layers, "seq_len": T, "q_heads": Hq,
+                  "kv_heads": w.n_kv_heads, "head_dim": d},
+        "bits_per_elem": round(plan.bits_per_elem(True), 4),
+        "bits_per_elem_containers_only": round(plan.bits_per_elem(False), 4),
+        "bytes_per_step": step_bytes, "rotated_copies": copies,
+        "step_ms": round(ms, 4), "gb_per_s": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+        "decode_tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+        "kv_token_layers_per_s": round(S * T / (ms * 1e-3), 1),
+        "kernel": kernel_name(w), "kernel_ms": round(kernel_ms, 4),
+        "kernel_bytes": kernel_bytes, "kernel_gb_per_s": round(kgbs, 2),
+        "kernel_frac_of_hbm_peak": round(kgbs / HBM_PEAK_GBS, 4),
+        "kernel_alu_tops": round(alu, 3), "kernel_frac_of_alu_peak": round(alu / VALU_PEAK_TOPS, 4),
+        "encode_ms": round(encode_ms, 3), "encode_token_layers_per_s": round(S * T / (encode_ms * 1e-3), 1),
+        "drift_stats": {"k_fallbacks": stats_once[0] + stats_once[1], "k_changed": stats_once[2],
+                        "k_overruns": stats_once[3], "v_fallbacks": stats_once[4] + stats_once[5],
+                        "v_changed": stats_once[6], "v_overruns": stats_once[7], "symbols_per_side": S * T * n,
+                        "k_changed_frac": round(stats_once[2] / (S * T * n), 6),
+                        "v_changed_frac": round(stats_once[6] / (S * T * n), 6)},
+    }
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if stream_ok:
+        # streaming decode: a compressed prefix of T - W tokens plus a bf16 tail of
+        # W - 1 tokens, and the append of one W-token window per sequence
+        n_pre, r_len = T - W, W - 1
+        ws_ex = torch.empty(plan.workspace_bytes(1, S, n_pre, Hq), dtype=torch.uint8, device=dev)
+
+        def step_ex(i):
+            kvq.kvq_decode_attention_ex(plan, q, caches[i % copies], n_pre, win_k16, win_v16, r_len,
+                                        out, ws_ex)
+
+        for i in range(args.warmup):
+            step_ex(i)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            step_ex(i)
+        t1.record()
+        torch.cuda.synchronize()
+        ex_ms = t0.elapsed_time(t1) / args.steps
+        ex_bytes = S * n_pre * (ck + cv + 8) + S * (n_pre // W) * (n + 2) + S * r_len * n * 2 * 2
+        reps = 3
+        kvq.kvq_encode_append(plan, win_k, win_v, cache, T - W)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            kvq.kvq_encode_append(plan, win_k, win_v, cache, T - W)
+        t1.record()
+        torch.cuda.synchronize()
+        app_ms = t0.elapsed_time(t1) / reps
+        rec["streaming"] = {"prefix_tokens": n_pre, "bf16_tail_tokens": r_len,
+                            "step_ms": round(ex_ms, 4), "step_gb_per_s": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 2),
+                            "append_window_ms": round(app_ms, 3),
+                            "append_token_layers_per_s": round(S * W / (app_ms * 1e-3), 1)}
+        log(f"[bench]   streaming: prefix {n_pre} + bf16 tail {r_len}: {ex_ms:.3f} ms/step; append of one "
+            f"{W}-token window per sequence {app_ms:.3f} ms")
+    if fw is not None:
+        plan_fw, cache_fw, fk, fv = fw
+        ws_fw = torch.empty(plan_fw.workspace_bytes(1, S, T, Hq), dtype=torch.uint8, device=dev)
+
+        def step_fw():
+            kvq.kvq_decode_attention_fixed_width(plan_fw, q, cache_fw["k_cont"], cache_fw["v_cont"],
+                                                 cache_fw["k_so"], cache_fw["v_so"], cache_fw["k_mean_q"],
+                                                 cache_fw["k_mean_scale"], out, ws_fw)
+
+        for _ in range(args.warmup):
+            step_fw()
+        torch.cuda.synchronize()
+        kvq.kvq_timing_collect()
+        kvq.kvq_timing_enable(True)
+        t0.record()
+        for _ in range(args.steps):
+            step_fw()
+        t1.record()
+        torch.cuda.synchronize()
+        kvq.kvq_timing_enable(False)
+        fw_ms = t0.elapsed_time(t1) / args.steps
+        fkms, fkl = kvq.kvq_timing_collect()
+        fw_kernel_ms = fkms / max(1, fkl)
+        fw_kernel_bytes = S * T * (fk + fv + 8)
+        charged = (n * (math.log2(6) + math.log2(3)) / 8 + 8 + (n + 2) / 128) * 8 / (2 * n)
+        rec["comparator_fixed_width"] = {
+            "levels": [6, 3], "containers": [fk, fv],
+            "bits_per_elem_stored": round(plan_fw.bits_per_elem(True), 4),
+            "bits_per_elem_charged_ideal": round(charged, 4),
+            "step_ms": round(fw_ms, 4), "kernel_ms": round(fw_kernel_ms, 4),
+            "kernel_gb_per_s": round(fw_kernel_bytes / (fw_kernel_ms * 1e-3) / 1e9, 2),
+            "kernel_frac_of_hbm_peak": round(fw_kernel_bytes / (fw_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "token_layers_per_s": round(S * T / (fw_ms * 1e-3), 1)}
+        log(f"[bench]   fixed-width 6/3 comparator: step {fw_ms:.3f} ms, kernel {fw_kernel_ms:.3f} ms")
+    del caches, cache, ws, out
+    if fw is not None:
+        del fw, cache_fw
+    torch.cuda.empty_cache()
+    return rec, samples
+
+
+def cpu_baseline(w, bi, samples):
+    """The oracle, as it stands, on a bounded sample of the headline workload:
+    both legs (Algorithm 1 + rANS encode; Algorithm 2 decode + float64
+    attention), in one single-threaded worker process per host core."""
+    import oracle as O
+    from kv_cache_entropy_amd import synth
+    from tests.oracle_pool import encode_cache_parallel, n_workers, time_decode_attention
+    ck, cv = w.containers[bi]
+    d = w.head_dim
+    p = O.OracleParams(w.n_kv_heads, d, 8, 6, ck, cv, 128, 1.4)
+    saved = {key: os.environ.get(key) for key in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for key in saved:
+        os.environ[key] = "1"
+    procs = n_workers()
+    try:
+        t_enc = time.perf_counter()
+        refs_full = [encode_cache_parallel(kk, vv, p, procs=procs) for kk, vv in zip(samples["k"], samples["v"])]
+        enc_s = time.perf_counter() - t_enc
+        enc_token_layers = sum(kk.shape[0] for kk in samples["k"])
+        nt = samples["tokens"]
+        refs = [{key: (r[key][:nt] if key in ("k_cont", "v_cont", "k_so", "v_so") else
+                       r[key][:nt // 128] if key in ("mu_hat", "k_mean_q", "k_mean_scale") else r[key])
+                 for key in r} for r in refs_full]
+        dt, tasks, _ = time_decode_attention(refs, samples["q"], p, procs, target_s=8.0)
+    finally:
+        for key, val in saved.items():
+            if val is None:
+                os.environ.pop(key, None)
+            else:
+                os.environ[key] = val
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
+    n = w.n
+    sample_bytes_one = nt * (ck + cv + 8) + (nt // 128) * (n + 2)
+    dec_tl_s = nt * tasks / dt
+    enc_tl_s = enc_token_layers / enc_s
+    extrap = {}
+    for name, wl in synth.WORKLOADS.items():
+        for b, (c_k, c_v) in zip(wl.budgets, wl.containers):
+            tl = wl.n_seqs * wl.seq_len
+            scale = wl.n_q_heads / w.n_q_heads      # the read side's attention work grows with the query heads
+            extrap[f"{name}@{b}"] = {"token_layers": tl, "encode_s": round(tl / enc_tl_s, 1),
+                                     "decode_attention_step_s": round(tl / dec_tl_s * max(1.0, scale), 2)}
+    return {"value": sample_bytes_one * tasks / dt / 1e9, "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "cpu": cpu_model,
+            "sample": f"read side: {tasks} decode-attention tasks of one sequence each ({nt} tokens, sequences "
+                      f"{samples['seqs']} of {w.name}, all {w.n_q_heads} query heads), {dt:.1f} s wall; "
+                      f"write side: Algorithm 1 + rANS on {enc_token_layers} token-layers of the same sequences "
+                      f"({samples['enc_tokens']} tokens each), {enc_s:.1f} s wall; {procs} single-threaded "
+                      f"worker processes",
+            "decode_attention_token_layers_per_s": round(dec_tl_s, 1),
+            "encode_token_layers_per_s": round(enc_tl_s, 1),
+            "extrapolated_full_config_seconds": extrap,
+            "extrapolation": "EXTRAPOLATED from the two sample rates above, linearly in token-layers (decode "
+                             "scaled by query heads relative to the sample); not measured"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,6 +364,8 @@ def main():
     ap.add_argument("--budget", type=float, default=None, help="bits/elem of the workload to run")
     ap.add_argument("--encode-reps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the chosen workload (no per-config block of the other workloads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -100,266 +395,68 @@ def main():
         bi = min(range(len(w.budgets)), key=lambda i: abs(w.budgets[i] - args.budget))
     elif 2.26 in w.budgets:
         bi = w.budgets.index(2.26)
+    head, samples = run_config(torch, kvq, synth, w, bi, args, dev, extras=True,
+                               cpu_sample=not args.no_cpu_baseline)
+    configs = []
+    if not args.no_configs:
+        for name, wl in synth.WORKLOADS.items():
+            for b in range(len(wl.budgets)):
+                if name == w.name and b == bi:
+                    continue
+                rec, _ = run_config(torch, kvq, synth, wl, b, args, dev)
+                configs.append(rec)
     ck, cv = w.containers[bi]
-    S, T, n, Hq, d = w.n_seqs, w.seq_len, w.n, w.n_q_heads, w.head_dim
-    plan = kvq.Plan(w.n_kv_heads, d, 8, 6, ck, cv, 128, 1.4)
-    nW = T // 128
-    log(f"[bench] workload={w.name} S={S} T={T} Hq={Hq} Hkv={w.n_kv_heads} C=({ck},{cv})")
-
-    # ---- seeded inputs, resident in HBM
-    kdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    k = torch.empty(S, T, n, dtype=kdt, device=dev)
-    v = torch.empty(S, T, n, dtype=kdt, device=dev)
-    for s in range(S):
-        ks, vs = synth.sequence_kv(w, s, dev)
-        k[s].copy_(ks)
-        v[s].copy_(vs)
-    q = synth.queries(w, dev)
-    torch.cuda.synchronize()
-    log("[bench] inputs generated")
-
-    # ---- write side
-    cache = kvq.alloc_cache(plan, S, T, dev)
-    stats = torch.zeros(8, dtype=torch.int64, device=dev)
-
-    def encode():
-        kvq.kvq_encode_streams(plan, k, v, cache["k_cont"], cache["v_cont"], cache["k_so"],
-                               cache["v_so"], cache["k_mean_q"], cache["k_mean_scale"], stats=stats)
-
-    encode()
-    torch.cuda.synchronize()
-    stats_once = stats.cpu().tolist()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.encode_reps):
-        encode()
-    e1.record()
-    torch.cuda.synchronize()
-    encode_ms = e0.elapsed_time(e1) / args.encode_reps
-    log(f"[bench] encode {encode_ms:.1f} ms for {S * T} token-layers")
-    # the fixed-width comparator of the same cache (page Appendix B: same
-    # preprocessing, nearest rounding at 6/3 levels, power-of-two widths)
-    fw_cmp = None
-    if w.n % 1024 == 0 and w.dtype == "bf16":
-        fk, fv = kvq.kvq_fixed_width_container_bytes(6, n), kvq.kvq_fixed_width_container_bytes(3, n)
-        plan_fw = kvq.Plan(w.n_kv_heads, d, 6, 3, fk, fv, 128, 1.4)
-        cache_fw = kvq.alloc_cache(plan_fw, S, T, dev)
-        kvq.kvq_encode_fixed_width(plan_fw, k, v, cache_fw["k_cont"], cache_fw["v_cont"], cache_fw["k_so"],
-                                   cache_fw["v_so"], cache_fw["k_mean_q"], cache_fw["k_mean_scale"])
-        torch.cuda.synchronize()
-    # samples for the CPU baseline, copied before the inputs are freed
-    base_seqs = [0, S - 1] if S > 1 else [0]
-    base_tokens = min(T, 512)
-    base_k = [k[s, :base_tokens].float().cpu().numpy() for s in base_seqs]
-    base_v = [v[s, :base_tokens].float().cpu().numpy() for s in base_seqs]
-    base_q = [q[s].float().cpu().numpy() for s in base_seqs]
-    # the last key-mean window of every sequence, for the streaming measurements
-    W = 128
-    stream_ok = T >= 2 * W
-    if stream_ok:
-        win_k = k[:, T - W:].contiguous()
-        win_v = v[:, T - W:].contiguous()
-        win_k16 = win_k.to(torch.bfloat16)
-        win_v16 = win_v.to(torch.bfloat16)
-    del k, v
-    torch.cuda.empty_cache()
-
-    # ---- read side: rotate copies when the working set would sit in cache
-    step_bytes = S * T * (ck + cv + 8) + S * nW * (n + 2)
-    kernel_bytes = S * T * (ck + cv + 8)
-    copies = max(1, math.ceil((1 << 30) / step_bytes))
-    caches = [cache] + [{key: t.clone() for key, t in cache.items()} for _ in range(copies - 1)]
-    ws = torch.empty(plan.workspace_bytes(1, S, T, Hq), dtype=torch.uint8, device=dev)
-    out = torch.empty(S, Hq, d, dtype=torch.bfloat16, device=dev)
-
-    def step(i):
-        c = caches[i % copies]
-        kvq.kvq_decode_attention(plan, q, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
-                                 c["k_mean_q"], c["k_mean_scale"], out, ws)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    kvq.kvq_timing_collect()
-    kvq.kvq_timing_enable(True)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    kvq.kvq_timing_enable(False)
-    ms = t0.elapsed_time(t1) / args.steps
-    kms, klaunch = kvq.kvq_timing_collect()
-    kernel_ms = kms / max(1, klaunch)
-    value = step_bytes / (ms * 1e-3) / 1e9
-    achieved = kernel_bytes / (kernel_ms * 1e-3) / 1e9
-    kernel_symbols = S * T * 2 * w.n
-    kernel_ops = kernel_symbols * DECODE_OPS_PER_SYMBOL
-    alu_achieved = kernel_ops / (kernel_ms * 1e-3) / 1e12
-    log(f"[bench] step {ms:.3f} ms ({value:.1f} GB/s); attention kernel {kernel_ms:.3f} ms "
-        f"({achieved:.1f} GB/s) over {klaunch} launches")
-
-    traffic = measured_traffic(f"{w.name}@{ck}/{cv}", kernel_bytes)
-
-    # ---- streaming decode: a compressed prefix of T - W tokens plus a bf16 tail
-    # of W - 1 tokens, and the append of one W-token window per sequence
-    streaming = None
-    if stream_ok:
-        n_pre, r_len = T - W, W - 1
-        ws_ex = torch.empty(plan.workspace_bytes(1, S, n_pre, Hq), dtype=torch.uint8, device=dev)
-
-        def step_ex(i):
-            kvq.kvq_decode_attention_ex(plan, q, caches[i % copies], n_pre, win_k16, win_v16, r_len,
-                                        out, ws_ex)
-
-        for i in range(args.warmup):
-            step_ex(i)
-        torch.cuda.synchronize()
-        t0.record()
-        for i in range(args.steps):
-            step_ex(i)
-        t1.record()
-        torch.cuda.synchronize()
-        ex_ms = t0.elapsed_time(t1) / args.steps
-        ex_bytes = S * n_pre * (ck + cv + 8) + S * (n_pre // W) * (n + 2) + S * r_len * n * 2 * 2
-        reps = 3
-        kvq.kvq_encode_append(plan, win_k, win_v, cache, T - W)
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(reps):
-            kvq.kvq_encode_append(plan, win_k, win_v, cache, T - W)
-        t1.record()
-        torch.cuda.synchronize()
-        app_ms = t0.elapsed_time(t1) / reps
-        streaming = {"prefix_tokens": n_pre, "bf16_tail_tokens": r_len,
-                     "step_ms": round(ex_ms, 4), "step_gb_per_s": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 2),
-                     "append_window_ms": round(app_ms, 3),
-                     "append_token_layers_per_s": round(S * W / (app_ms * 1e-3), 1)}
-        log(f"[bench] streaming: prefix {n_pre} + bf16 tail {r_len}: {ex_ms:.3f} ms/step; "
-            f"append of one {W}-token window per sequence {app_ms:.3f} ms")
-
-    if w.n % 1024 == 0 and w.dtype == "bf16":
-        ws_fw = torch.empty(plan_fw.workspace_bytes(1, S, T, Hq), dtype=torch.uint8, device=dev)
-
-        def step_fw():
-            kvq.kvq_decode_attention_fixed_width(plan_fw, q, cache_fw["k_cont"], cache_fw["v_cont"],
-                                                 cache_fw["k_so"], cache_fw["v_so"], cache_fw["k_mean_q"],
-                                                 cache_fw["k_mean_scale"], out, ws_fw)
-
-        for _ in range(args.warmup):
-            step_fw()
-        torch.cuda.synchronize()
-        kvq.kvq_timing_collect()
-        kvq.kvq_timing_enable(True)
-        t0.record()
-        for _ in range(args.steps):
-            step_fw()
-        t1.record()
-        torch.cuda.synchronize()
-        kvq.kvq_timing_enable(False)
-        fw_ms = t0.elapsed_time(t1) / args.steps
-        fkms, fkl = kvq.kvq_timing_collect()
-        fw_kernel_ms = fkms / max(1, fkl)
-        fw_kernel_bytes = S * T * (fk + fv + 8)
-        charged = (n * (math.log2(6) + math.log2(3)) / 8 + 8 + (n + 2) / 128) * 8 / (2 * n)
-        fw_cmp = {"levels": [6, 3], "containers": [fk, fv],
-                  "bits_per_elem_stored": round(plan_fw.bits_per_elem(True), 4),
-                  "bits_per_elem_charged_ideal": round(charged, 4),
-                  "step_ms": round(fw_ms, 4), "kernel_ms": round(fw_kernel_ms, 4),
-                  "kernel_gb_per_s": round(fw_kernel_bytes / (fw_kernel_ms * 1e-3) / 1e9, 2),
-                  "kernel_frac_of_hbm_peak": round(fw_kernel_bytes / (fw_kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                  "token_layers_per_s": round(S * T / (fw_ms * 1e-3), 1)}
-        log(f"[bench] fixed-width 6/3 comparator: step {fw_ms:.3f} ms, kernel {fw_kernel_ms:.3f} ms "
-            f"({fw_cmp['kernel_gb_per_s']:.1f} GB/s of {fk + fv} B containers)")
-        del cache_fw
-
-    # ---- CPU baseline: the oracle's read side on a bounded sample
-    cpu = None
-    if not args.no_cpu_baseline:
-        import numpy as np  # noqa: F401
-        import oracle as O
-        from tests.oracle_pool import encode_cache_parallel, n_workers, time_decode_attention
-        p = O.OracleParams(w.n_kv_heads, d, 8, 6, ck, cv, 128, 1.4)
-        # one worker process per host core, each single-threaded (no nested
-        # BLAS threads); the spawned workers inherit these settings
-        saved = {key: os.environ.get(key) for key in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
-                                                      "MKL_NUM_THREADS")}
-        for key in saved:
-            os.environ[key] = "1"
-        try:
-            refs = [encode_cache_parallel(kk, vv, p) for kk, vv in zip(base_k, base_v)]
-            procs = n_workers()
-            sample_bytes_one = base_tokens * (ck + cv + 8) + (base_tokens // 128) * (n + 2)
-            dt, tasks, _ = time_decode_attention(refs, base_q, p, procs, target_s=8.0)
-        finally:
-            for key, val in saved.items():
-                if val is None:
-                    os.environ.pop(key, None)
-                else:
-                    os.environ[key] = val
-        cpu_model = "unknown"
-        try:
-            with open("/proc/cpuinfo") as fh:
-                cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
-                                 cpu_model)
-        except OSError:
-            pass
-        cpu = {"value": sample_bytes_one * tasks / dt / 1e9, "unit": "GB/s", "cores": procs,
-               "kind": "oracle", "cpu": cpu_model,
-               "sample": f"{tasks} decode-attention tasks of one sequence each ({base_tokens} tokens, "
-                         f"sequences {base_seqs} of this workload, all {Hq} query heads): Algorithm-2 "
-                         f"decode + float64 attention in {procs} single-threaded worker processes; "
-                         f"{dt:.1f} s wall"}
-        log(f"[bench] cpu oracle {cpu['value'] * 1e3:.3f} MB/s on {procs} cores")
-
+    traffic = measured_traffic(f"{w.name}@{ck}/{cv}", head["kernel_bytes"])
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, bi, samples)
+    if cpu:
+        log(f"[bench] cpu oracle: read side {cpu['value'] * 1e3:.3f} MB/s, encode "
+            f"{cpu['encode_token_layers_per_s']:.0f} token-layers/s on {cpu['cores']} cores")
+    S, T = w.n_seqs, w.seq_len
     rec = {
         "metric": "fused dequant+decode-attention compressed-KV throughput",
-        "value": round(value, 2),
+        "value": head["gb_per_s"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": head["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u32 rANS decode + fp32 attention",
         "data": "synthetic (seeded; stands in for captured KV of a trained model)",
         "config": {
-            "workload": f"{w.name}: {Hq} q / {w.n_kv_heads} kv heads, d={d}, batch {w.batch}, "
+            "workload": f"{w.name}: {w.n_q_heads} q / {w.n_kv_heads} kv heads, d={w.head_dim}, batch {w.batch}, "
                         f"{w.layers} layers, context {T}, {ck}/{cv}-byte containers, 8/6 levels",
             "global_batch": w.batch, "seq_len": T, "layers": w.layers,
-            "bits_per_elem": round(plan.bits_per_elem(True), 4),
-            "bits_per_elem_containers_only": round(plan.bits_per_elem(False), 4),
+            "bits_per_elem": head["bits_per_elem"],
+            "bits_per_elem_containers_only": head["bits_per_elem_containers_only"],
             "parallelism": "single GPU",
         },
-        "decode_tokens_per_s": round(w.batch / (ms * 1e-3), 1),
-        "kv_token_layers_per_s": round(S * T / (ms * 1e-3), 1),
-        "bytes_per_step": step_bytes,
-        "encode_ms": round(encode_ms, 3),
-        "encode_token_layers_per_s": round(S * T / (encode_ms * 1e-3), 1),
-        "drift_stats": {"k_fallbacks": stats_once[0] + stats_once[1], "k_changed": stats_once[2],
-                        "k_overruns": stats_once[3], "v_fallbacks": stats_once[4] + stats_once[5],
-                        "v_changed": stats_once[6], "v_overruns": stats_once[7],
-                        "symbols_per_side": S * T * n},
-        "rotated_copies": copies,
-        "streaming": streaming,
-        "comparator_fixed_width": fw_cmp,
-        # The fused kernel is bound by plain integer ALU work (rANS decode), not
-        # by HBM: achieved = minimal decode operations per launch / its time,
-        # against the VALU peak; the HBM view of the same launch is kept below.
-        "roofline": {"bound": "alu", "achieved": round(alu_achieved, 3),
-                     "peak": round(VALU_PEAK_TOPS, 3), "unit": "Tops/s",
-                     "frac": round(alu_achieved / VALU_PEAK_TOPS, 4),
-                     "traffic": traffic,
-                     "kernel": "attention4_kernel", "kernel_ms": round(kernel_ms, 4),
-                     "algorithmic_ops_per_launch": kernel_ops,
-                     "ops_per_symbol": DECODE_OPS_PER_SYMBOL, "symbols_per_launch": kernel_symbols,
-                     "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(achieved / HBM_PEAK_GBS, 4),
-                             "algorithmic_bytes_per_launch": kernel_bytes}},
+        "decode_tokens_per_s": head["decode_tokens_per_s"],
+        "kv_token_layers_per_s": head["kv_token_layers_per_s"],
+        "bytes_per_step": head["bytes_per_step"],
+        "encode_ms": head["encode_ms"],
+        "encode_token_layers_per_s": head["encode_token_layers_per_s"],
+        "drift_stats": head["drift_stats"],
+        "rotated_copies": head["rotated_copies"],
+        "streaming": head.get("streaming"),
+        "comparator_fixed_width": head.get("comparator_fixed_width"),
+        # The metric's roofline: algorithmic compressed bytes of one launch of the
+        # fused kernel over its average duration (HIP events on its stream),
+        # against MI355X HBM peak.  The plain-ALU view (the decode operations the
+        # rANS format needs per symbol, against the VALU peak) binds first; it is
+        # kept beside it.
+        "roofline": {"bound": "hbm", "achieved": head["kernel_gb_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["kernel_frac_of_hbm_peak"], "traffic": traffic,
+                     "kernel": head["kernel"], "kernel_ms": head["kernel_ms"],
+                     "algorithmic_bytes_per_launch": head["kernel_bytes"],
+                     "gap_to_60pct_target": round(0.6 / head["kernel_frac_of_hbm_peak"], 2),
+                     "alu": {"achieved": head["kernel_alu_tops"], "peak": round(VALU_PEAK_TOPS, 3),
+                             "unit": "Tops/s", "frac": head["kernel_frac_of_alu_peak"],
+                             "ops_per_symbol": DECODE_OPS_PER_SYMBOL,
+                             "symbols_per_launch": S * T * 2 * w.n}},
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
