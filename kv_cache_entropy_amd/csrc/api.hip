@@ -20,11 +20,19 @@ size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Split-K geometry of the decode attention: 64-token tiles; enough splits to
 // give the chip about 2048 waves (each split is one wave).
-void split_geometry(int64_t S, int64_t T, int* nsplit, int64_t* tokens_per_split) {
+// one_tile: every split holds one 64-token tile (the fused kernel for 8 query
+// heads on more than 2 KV heads writes each head's partial output right after
+// its tile, so it needs splits of one tile).
+void split_geometry(int64_t S, int64_t T, int* nsplit, int64_t* tokens_per_split, bool one_tile = false) {
   const int64_t tiles = T / 64;
   if (tiles == 0) {
     *nsplit = 0;
     *tokens_per_split = 0;
+    return;
+  }
+  if (one_tile) {
+    *tokens_per_split = 64;
+    *nsplit = int(tiles);
     return;
   }
   int64_t want = (2048 + S - 1) / S;
@@ -42,13 +50,15 @@ struct WsLayout {
 // Decode-attention workspace: the fp16 query operand (hi + lo, 16 bytes per
 // 4 channels of a query slot; slots padded to a multiple of 4 per KV head),
 // per-head scale, sum and per-window mean terms, and the split partials.
+bool one_tile_splits(int G, int hkv) { return G == 8 && hkv > 2; }
+
 WsLayout ws_layout(const kvq_plan* plan, int64_t S, int64_t T, int Hq) {
   int nsplit;
   int64_t tps;
-  split_geometry(S, T, &nsplit, &tps);
   const int d = plan->params.head_dim;
   const int hkv = plan->params.n_kv_heads;
   const int G = Hq / hkv > 0 ? Hq / hkv : 1;
+  split_geometry(S, T, &nsplit, &tps, one_tile_splits(G, hkv));
   const int slots = ((G + 3) / 4) * 4;
   const int64_t nW = T / plan->params.mean_window;
   WsLayout w;
@@ -300,7 +310,7 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
   if (workspace_bytes < wl.total) return KVQ_EWORKSPACE;
   int nsplit;
   int64_t tps;
-  split_geometry(n_seqs, n_tokens, &nsplit, &tps);
+  split_geometry(n_seqs, n_tokens, &nsplit, &tps, one_tile_splits(G, Hkv));
   const int part_splits = nsplit + (res_len > 0 ? 1 : 0);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);

@@ -1199,6 +1199,10 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   constexpr bool PERM = Lay::PERM;
   constexpr int RS = Lay::RS;
   constexpr uint32_t TAB = PERM ? Lay::P_TAB : 0u;
+  // 8 query heads on more than 2 KV heads: the accumulators of all heads would
+  // not fit the registers, so every split holds one tile (the host sets that
+  // geometry) and the V wave writes each head's output right after its step.
+  constexpr bool PERHEAD = G == 8 && HKV > 2;
   __shared__ __align__(16) uint8_t lds[Lay::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -1457,6 +1461,66 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   const uint32_t misV = uint32_t(reinterpret_cast<uintptr_t>(vseq) & 15u);
   uint32_t xv = 0;
   int buf = 0;
+  if constexpr (PERHEAD) {
+    for (int64_t i = 0; i < NT; ++i) {                  // NT == 1
+      const int64_t tV = tb + 64 * i;
+#pragma unroll 1
+      for (int g = 0; g < HKV; ++g) {
+        step_barrier();                                 // the K wave's weights of (i, g)
+        if (g == 0) xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
+        const uint16_t* const wv = wts + buf * (Lay::WTS_BUF / 2);
+        const uint16_t* const wv_lo = wv + NW * 64;
+        float4_t Oc[2][NGM];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int m = 0; m < NGM; ++m) Oc[c][m] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll 1
+          for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+            for (int bh = 0; bh < 2; ++bh) {
+              const int b4 = 2 * b2 + bh;
+              if (bh == 1) ring5_block<1, RS>(rv, lds, rsV);
+              else ring5_block<0, RS>(rv, lds, rsV);
+#pragma unroll
+              for (int cc = 0; cc < 4; ++cc) {
+                const uint32_t winV = ring5_window<RS>(rv, lds);
+                uint32_t selv = kSel0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const uint32_t ev = dec5_step<PERM, Lay::SLOT_SHIFT, TAB>(xv, winV, selv, lds, toffV);
+                  vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
+                }
+                rv.P += selv - kSel0;
+              }
+            }
+          wave_lds_fence();
+          if (lo_levels)
+            pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, Oc[ch]);
+          else
+            pv_half_int<NGM>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, Oc[ch]);
+          wave_lds_fence();
+        }
+        buf ^= 1;
+        // the split's only tile: this head's accumulators are final
+#pragma unroll
+        for (int m = 0; m < NGM; ++m)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int v = m * 4 + ii;
+            if (v < G) {
+              const int h = g * G + v;
+#pragma unroll
+              for (int c = 0; c < 2; ++c) P[h * (kD + 4) + c * 64 + lane] = Oc[c][m][ii];
+            }
+          }
+      }
+    }
+    for (int64_t k = NT * HKV; k < nsteps_all; ++k) step_barrier();
+    return;
+  }
   for (int64_t i = 0; i < NT; ++i) {
     const int64_t tV = tb + 64 * i;
 #pragma unroll 1
@@ -1815,9 +1879,11 @@ template <int G, int HKV>
 static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stream) {
   // the interleaved kernel keeps V levels as int8 and maps them to fp16 with
   // an 8-entry lookup, so it serves V alphabets of up to 8 levels
-  constexpr bool kSplit = kUseSplitWaves && (G <= 4 || HKV <= 2);
+  constexpr bool kSplit = kUseSplitWaves;
   if constexpr (kSplit) {
     if (a.Mv <= 8) {
+      // 8 query heads on more than 2 KV heads need splits of one tile
+      if (G == 8 && HKV > 2 && a.tokens_per_split != 64) return hipErrorInvalidValue;
       const int64_t pairs = S * a.nsplit;
       constexpr int64_t kCUs = 256;
       int64_t ppw = (pairs + kCUs - 1) / kCUs;
