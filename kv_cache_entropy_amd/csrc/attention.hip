@@ -1119,9 +1119,9 @@ struct Lay5 {
   static constexpr int NW = ((G + 3) / 4) * 4;
   static constexpr uint32_t VCH = 0;
   static constexpr uint32_t WTS = 64u * kChunk8Stride;
-  static constexpr uint32_t WTS_BUF = 2u * NW * 64u * 2u;
-  static constexpr uint32_t ALV = WTS + 2u * WTS_BUF;              // 2 x [16] f32 (NW factors, flag at 15)
-  static constexpr uint32_t RUN = ALV + 2u * 64u;                  // 6 x [HQ] f32
+  static constexpr uint32_t WTS_BUF = 2u * NW * 64u * 2u;        // fp16 hi and lo weights of one step
+  static constexpr uint32_t ALV = WTS + WTS_BUF;                   // [16] f32 (NW factors, flag at 15)
+  static constexpr uint32_t RUN = ALV + 64u;                       // 6 x [HQ] f32
   static constexpr uint32_t SIZE = (RUN + 6u * HQ * 4u + 15u) & ~15u;
   static constexpr uint32_t RINGS = (kPairs * SIZE + 255u) & ~255u;
   static constexpr uint32_t RING_END = RINGS + 2u * kPairs * kRingBytes;
@@ -1144,7 +1144,7 @@ struct Lay5 {
   // in 512-byte rows shared by two rings (one at bytes 0 and 256, one at 128
   // and 384), and the free half of the last of them holds each pair's running
   // max, sums and rescale factors, 128 bytes apiece (HQ <= 32).
-  static constexpr uint32_t P_AFF = WTS + 2u * WTS_BUF;       // per pair: VCH, WTS, affine terms
+  static constexpr uint32_t P_AFF = WTS + WTS_BUF;            // per pair: VCH, WTS, affine terms
   static constexpr uint32_t P_SIZE = (P_AFF + 3u * HQ * 4u + 15u) & ~15u;
   static constexpr uint32_t P_TAB = (kPairs * P_SIZE + 255u) & ~255u;
   static constexpr uint32_t P_RING_BYTES = 17u * 512u;
@@ -1160,14 +1160,34 @@ struct Lay5 {
                                4 * kPairs <= 34 && P_TOTAL <= 163840u && P_TAB <= 65535u;
   static constexpr uint32_t LDS_BYTES = PERM ? P_TOTAL : TOTAL;
   static constexpr int RS = PERM ? 9 : 8;
+  // pair p's rescale factors: [16] f32 (NW <= 8 factors, the flag at 15);
+  // dwords 12 and 13 hold the pair's hand-off counters
+  static constexpr uint32_t alv_off(int p) { return PERM ? piece(4 * p + 3) : uint32_t(p) * SIZE + ALV; }
+  static constexpr uint32_t READY = 12u * 4u, DONE = 13u * 4u;
 };
 
-// s_barrier with only LDS traffic ordered around it: container loads in
-// flight stay in flight.
-__device__ __forceinline__ void step_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
+// Hand-off between the two waves of a pair through two LDS step counters,
+// so that pairs never wait for one another (a workgroup barrier would hold
+// every pair to the slowest one at each step).  The K wave posts `ready` =
+// j + 1 once the weights of its step j are in LDS; the V wave posts `done` =
+// j + 1 once it has read them.  Only LDS accesses are ordered around the
+// counters: container loads in flight stay in flight.  The wait is bounded
+// (about 2^20 sleeps of 64 clocks, far beyond any step) so that no wave can
+// spin for ever; both waves of a pair run the same step sequence, so the
+// bound is never reached in a correct run.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ void pair_wait(const uint32_t* counter, uint32_t want) {
+  for (uint32_t it = 0; it < kSpinLimit; ++it) {
+    if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= want) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ void pair_post(uint32_t* counter, uint32_t value, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if (lane == 0) __hip_atomic_store(counter, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // pv_half for integer V levels (every fp16 level has a zero low byte): one
@@ -1228,6 +1248,10 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
       reinterpret_cast<uint32_t*>(lds + Lay::TABV)[idx] = ev;
     }
   }
+  if (tid < int(blockDim.x >> 7)) {
+    *reinterpret_cast<uint32_t*>(lds + Lay::alv_off(tid) + Lay::READY) = 0u;
+    *reinterpret_cast<uint32_t*>(lds + Lay::alv_off(tid) + Lay::DONE) = 0u;
+  }
   __syncthreads();
 
   // lane offset of ring i (2 pw + stream)
@@ -1242,18 +1266,17 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   };
 
   const int64_t gp = int64_t(blockIdx.x) * (blockDim.x >> 7) + pw;
-  const int64_t nsteps_all = (a.tokens_per_split / 64) * HKV;
-  if (gp >= S * a.nsplit) {                // no split: only the workgroup's barriers
-    for (int64_t k = 0; k < nsteps_all; ++k) step_barrier();
-    return;
-  }
+  if (gp >= S * a.nsplit) return;          // no split for this pair
   const int64_t s = gp / a.nsplit;
   const int split = int(gp - s * a.nsplit);
 
   uint8_t* const mine = lds + uint32_t(pw) * (PERM ? Lay::P_SIZE : Lay::SIZE);
   uint8_t* const vch = mine + Lay::VCH;
   uint16_t* const wts = reinterpret_cast<uint16_t*>(mine + Lay::WTS);
-  float* const alv = reinterpret_cast<float*>(PERM ? lds + Lay::piece(4 * pw + 3) : mine + Lay::ALV);
+  float* const alv = reinterpret_cast<float*>(lds + Lay::alv_off(pw));
+  uint32_t* const ready = reinterpret_cast<uint32_t*>(lds + Lay::alv_off(pw) + Lay::READY);
+  uint32_t* const done = reinterpret_cast<uint32_t*>(lds + Lay::alv_off(pw) + Lay::DONE);
+  uint32_t step = 0;                  // steps of this wave so far (tile i, KV head g)
   float* const runM = reinterpret_cast<float*>(PERM ? lds + Lay::piece(4 * pw) : mine + Lay::RUN);
   float* const runL = PERM ? reinterpret_cast<float*>(lds + Lay::piece(4 * pw + 1)) : runM + HQ;
   float* const runZ = PERM ? reinterpret_cast<float*>(lds + Lay::piece(4 * pw + 2)) : runL + HQ;
@@ -1303,8 +1326,6 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
     const uint32_t misK = uint32_t(reinterpret_cast<uintptr_t>(kseq) & 15u);
     uint32_t xk = 0;
     float sk = 0.f, ok = 0.f, svK = 0.f, ovK = 0.f;
-    int buf = 0;
-
     for (int64_t i = 0; i < NT; ++i) {
       const int64_t tK = tb + 64 * i;
 #pragma unroll 1
@@ -1380,9 +1401,9 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
             }
         }
         // logits -> online softmax (lazy running maximum) -> weights of this step
-        uint16_t* const wk = wts + buf * (Lay::WTS_BUF / 2);
-        float* const al = alv + buf * 16;
         float sums[2 * G];
+        uint32_t wbits[NW];             // fp16 hi (low half) and lo (high half) weight
+        float alf[NW];
         bool grew = false;
 #pragma unroll
         for (int v = 0; v < NW; ++v) {
@@ -1409,18 +1430,25 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
             whi = wt;
             wlo = wt - __half2float(hh);
           }
-          wk[v * 64 + lane] = __half_as_ushort(__float2half_rn(whi));
-          wk[NW * 64 + v * 64 + lane] = __half_as_ushort(__float2half_rn(wlo));
-          if (lane == 0) al[v] = alh;
+          wbits[v] = uint32_t(__half_as_ushort(__float2half_rn(whi))) |
+                     (uint32_t(__half_as_ushort(__float2half_rn(wlo))) << 16);
+          alf[v] = alh;
         }
-        if (lane == 0) al[15] = grew ? 1.f : 0.f;
         const float tot = wave_sum_scatter<2 * G>(sums, lane);
         if (lane < 2 * G) atomicAdd(sum_slot + g * G, tot);
-        buf ^= 1;
-        step_barrier();
+        // one weight buffer per pair: free once the V wave has finished the
+        // previous step (it decodes the first half of its next step meanwhile)
+        pair_wait(done, step);
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+          wts[v * 64 + lane] = uint16_t(wbits[v]);
+          wts[NW * 64 + v * 64 + lane] = uint16_t(wbits[v] >> 16);
+          if (lane == 0) alv[v] = alf[v];
+        }
+        if (lane == 0) alv[15] = grew ? 1.f : 0.f;
+        pair_post(ready, ++step, lane);
       }
     }
-    for (int64_t k = NT * HKV; k < nsteps_all; ++k) step_barrier();
     wave_lds_fence();
 #pragma unroll
     for (int v = 0; v < G; ++v)
@@ -1460,15 +1488,13 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   const __amdgpu_buffer_rsrc_t rsV = seq_rsrc(vseq, uint32_t(a.T * a.CV));
   const uint32_t misV = uint32_t(reinterpret_cast<uintptr_t>(vseq) & 15u);
   uint32_t xv = 0;
-  int buf = 0;
   if constexpr (PERHEAD) {
     for (int64_t i = 0; i < NT; ++i) {                  // NT == 1
       const int64_t tV = tb + 64 * i;
 #pragma unroll 1
       for (int g = 0; g < HKV; ++g) {
-        step_barrier();                                 // the K wave's weights of (i, g)
         if (g == 0) xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
-        const uint16_t* const wv = wts + buf * (Lay::WTS_BUF / 2);
+        const uint16_t* const wv = wts;
         const uint16_t* const wv_lo = wv + NW * 64;
         float4_t Oc[2][NGM];
 #pragma unroll
@@ -1496,6 +1522,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
                 rv.P += selv - kSel0;
               }
             }
+          if (ch == 0) pair_wait(ready, step + 1u);     // the K wave's weights of (i, g)
           wave_lds_fence();
           if (lo_levels)
             pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, Oc[ch]);
@@ -1503,7 +1530,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
             pv_half_int<NGM>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, Oc[ch]);
           wave_lds_fence();
         }
-        buf ^= 1;
+        pair_post(done, ++step, lane);
         // the split's only tile: this head's accumulators are final
 #pragma unroll
         for (int m = 0; m < NGM; ++m)
@@ -1518,26 +1545,15 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
           }
       }
     }
-    for (int64_t k = NT * HKV; k < nsteps_all; ++k) step_barrier();
     return;
   }
   for (int64_t i = 0; i < NT; ++i) {
     const int64_t tV = tb + 64 * i;
 #pragma unroll 1
     for (int g = 0; g < HKV; ++g) {
-      step_barrier();                                   // the K wave's weights of (i, g)
       if (g == 0) xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
-      const uint16_t* const wv = wts + buf * (Lay::WTS_BUF / 2);
+      const uint16_t* const wv = wts;
       const uint16_t* const wv_lo = wv + NW * 64;
-      const float* const al = alv + buf * 16;
-      if (al[15] != 0.f) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int m = 0; m < NGM; ++m)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[0][c][m][ii] *= al[m * 4 + ii];
-      }
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll 1
@@ -1559,6 +1575,17 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
               rv.P += selv - kSel0;
             }
           }
+        if (ch == 0) {
+          pair_wait(ready, step + 1u);                  // the K wave's weights of (i, g)
+          if (alv[15] != 0.f) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int m = 0; m < NGM; ++m)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) O[0][c][m][ii] *= alv[m * 4 + ii];
+          }
+        }
         wave_lds_fence();
         if (lo_levels)
           pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[0][ch]);
@@ -1566,7 +1593,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
           pv_half_int<NGM>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, O[0][ch]);
         wave_lds_fence();
       }
-      buf ^= 1;
+      pair_post(done, ++step, lane);
       // rotate: the next step's head becomes O[0]
       if (HKV > 1) {
 #pragma unroll
@@ -1581,7 +1608,6 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
       }
     }
   }
-  for (int64_t k = NT * HKV; k < nsteps_all; ++k) step_barrier();
 #pragma unroll
   for (int g = 0; g < HKV; ++g)
 #pragma unroll
