@@ -53,15 +53,17 @@ __global__ __launch_bounds__(256) void decode_symbols_kernel(DecSymArgs a) {
 
 // ----------------------------------------------------------------- combine
 // One workgroup per (query head, sequence).  Its waves share the splits: each
-// merges a contiguous range (the max and per-split weights spread over the
-// lanes, the weighted sum of partial outputs over 64 splits at a time with
-// independent loads), then wave 0 merges the waves' results through LDS, undoes
-// the rotation and stores.  A single long sequence has thousands of splits:
-// then a first pass (FINAL = false, one workgroup per (query head, sequence,
-// group of `group` splits)) merges each group into the group's first slot, in
-// place (a group is read only by its own workgroup), and the final pass
-// merges those slots, `group` apart.
+// merges a contiguous range of at most kCombineChunk splits per round (the
+// maxima, sums and weights spread over the lanes, the partial outputs of the
+// whole round loaded before any is used, so that a round costs one memory
+// latency), then wave 0 merges the waves' results through LDS, undoes the
+// rotation and stores.  A single long sequence has thousands of splits: then a
+// first pass (FINAL = false, one workgroup per (query head, sequence, group of
+// `group` splits)) merges each group into the group's first slot, in place (a
+// group is read only by its own workgroup), and the final pass merges those
+// slots, `group` apart.
 constexpr int kCombineMaxWaves = 16;
+constexpr int kCombineChunk = 16;          // splits per wave and round
 constexpr int kCombineGroup = 64;          // splits per first-pass workgroup
 constexpr int kCombineTwoPass = 128;       // split counts above this take two passes
 
@@ -89,23 +91,31 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineA
 #pragma unroll
   for (int i = 0; i < NPL; ++i) acc[i] = 0.f;
   if (Mx > -__builtin_inff()) {
-    for (int k0 = kb; k0 < ke; k0 += 64) {
-      const int k = k0 + lane;
-      float sck = 0.f, lk = 0.f, zk = 0.f;
-      if (k < ke) {
-        const float* Pk = P + int64_t(k) * step * sp;
-        sck = __expf(Pk[a.d] - Mx);
-        lk = sck * Pk[a.d + 1];
-        zk = sck * Pk[a.d + 2];
+    for (int k0 = kb; k0 < ke; k0 += kCombineChunk) {
+      const int kn = ke - k0 < kCombineChunk ? ke - k0 : kCombineChunk;
+      // every load of the round first: lane j < kn the max and sums of split
+      // k0 + j, each lane its NPL channels of the kn partial outputs
+      float mk = -__builtin_inff(), lk = 0.f, zk = 0.f;
+      if (lane < kn) {
+        const float* Pk = P + int64_t(k0 + lane) * step * sp;
+        mk = Pk[a.d];
+        lk = Pk[a.d + 1];
+        zk = Pk[a.d + 2];
       }
-      L += wave_sum_f32(lk);
-      Z += wave_sum_f32(zk);
-      const int kn = ke - k0 < 64 ? ke - k0 : 64;
-#pragma unroll 8
-      for (int j = 0; j < kn; ++j) {
-        const float sc = __shfl(sck, j, 64);
+      float v[kCombineChunk][NPL];
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) acc[i] += sc * P[int64_t(k0 + j) * step * sp + lane * NPL + i];
+      for (int j = 0; j < kCombineChunk; ++j)
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+          v[j][i] = j < kn ? P[int64_t(k0 + j) * step * sp + lane * NPL + i] : 0.f;
+      const float sck = lane < kn ? __expf(mk - Mx) : 0.f;
+      L += wave_sum_f32(sck * lk);
+      Z += wave_sum_f32(sck * zk);
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j) {
+        const float sc = __shfl(sck, j, 64);            // 0 past kn
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) acc[i] += sc * v[j][i];
       }
     }
   }
@@ -290,11 +300,13 @@ static hipError_t launch_combine_t(const CombineArgs& a, int64_t S, hipStream_t 
   if (a.nsplit > kCombineTwoPass) {
     group = kCombineGroup;
     const dim3 grid1(a.Hq, unsigned(S), unsigned((a.nsplit + group - 1) / group));
-    hipLaunchKernelGGL((combine_kernel<NPL, false>), grid1, dim3(64), 0, stream, a, group);
+    hipLaunchKernelGGL((combine_kernel<NPL, false>), grid1, dim3(64 * (kCombineGroup / kCombineChunk)), 0, stream,
+                       a, group);
   }
-  // about 128 merged slots per wave, up to 16 waves per (query head, sequence)
+  // one round of kCombineChunk merged slots per wave, up to 16 waves per
+  // (query head, sequence)
   const int slots = (a.nsplit + group - 1) / group;
-  int waves = (slots + 127) / 128;
+  int waves = (slots + kCombineChunk - 1) / kCombineChunk;
   waves = waves < 1 ? 1 : (waves > kCombineMaxWaves ? kCombineMaxWaves : waves);
   hipLaunchKernelGGL((combine_kernel<NPL, true>), dim3(a.Hq, unsigned(S)), dim3(64 * waves), 0, stream, a, group);
   return hipGetLastError();
