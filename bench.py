@@ -451,7 +451,8 @@ def main():
                      "frac": head["kernel_frac_of_hbm_peak"], "traffic": traffic,
                      "kernel": head["kernel"], "kernel_ms": head["kernel_ms"],
                      "algorithmic_bytes_per_launch": head["kernel_bytes"],
-                     "gap_to_60pct_target": round(0.6 / head["kernel_frac_of_hbm_peak"], 2),
+                     "gap_to_60pct_target": round(0.6 * HBM_PEAK_GBS / head["kernel_gb_per_s"], 2)
+                     if head["kernel_gb_per_s"] > 0 else None,
                      "alu": {"achieved": head["kernel_alu_tops"], "peak": round(VALU_PEAK_TOPS, 3),
                              "unit": "Tops/s", "frac": head["kernel_frac_of_alu_peak"],
                              "ops_per_symbol": DECODE_OPS_PER_SYMBOL,

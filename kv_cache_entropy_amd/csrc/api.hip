@@ -372,6 +372,11 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
       aa.lbv[m] = plan->side[1].fp16_lo[m];
       if (aa.lbv[m]) aa.v_lo_nonzero = 1;
     }
+    for (int z = 0; z < 256; ++z) {
+      const uint32_t dk = plan->side[0].dec[z];
+      aa.tabk[z] = (dk & 0xFFFFu) | (plan->side[0].fp16_bits[(dk >> 16) & 0xFFu] << 16);
+      aa.tabv[z] = plan->side[1].dec[z];
+    }
     size_t slot = 0;
     const bool timed = timer_begin(stream, &slot);
     const hipError_t e = fixed_width ? kvq::launch_attention_fw(aa, n_seqs, n_q_heads, G, bk, bv, stream)

@@ -770,14 +770,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a,
 
   // decode tables, shared by the workgroup (PERM: 16 replicas per table in
   // each 256-byte row; otherwise REPS contiguous replicas per slot)
+  // Decode tables: entry idx of the replicated table is the host's entry for
+  // slot idx / NREP (one load from the kernel arguments).
   constexpr uint32_t NREP = PERM ? 16u : Lay::REPS;
+#pragma unroll 4
   for (int idx = tid; idx < 256 * int(NREP); idx += int(blockDim.x)) {
     const uint32_t z = uint32_t(idx) / NREP;
-    uint32_t mk = 0, mv = 0;
-    for (int m = 1; m < a.Mk; ++m) mk = (z >= a.ck[m]) ? uint32_t(m) : mk;
-    for (int m = 1; m < a.Mv; ++m) mv = (z >= a.cv[m]) ? uint32_t(m) : mv;
-    const uint32_t ek = a.fk[mk] | ((z - a.ck[mk]) << 8) | (a.lvk[mk] << 16);
-    const uint32_t ev = a.fv[mv] | ((z - a.cv[mv]) << 8) | (mv << 16);
+    const uint32_t ek = a.tabk[z], ev = a.tabv[z];
     if (PERM) {
       const uint32_t row = Lay::P_TAB + z * 256u + (uint32_t(idx) % NREP) * 4u;
       *reinterpret_cast<uint32_t*>(lds + row) = ek;
@@ -1231,14 +1230,13 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   const int pw = w >> 1;              // pair within the workgroup
   const bool kwave = (w & 1) == 0;
 
+  // Decode tables: entry idx of the replicated table is the host's entry for
+  // slot idx / NREP (one load from the kernel arguments).
   constexpr uint32_t NREP = PERM ? 16u : Lay::REPS;
+#pragma unroll 4
   for (int idx = tid; idx < 256 * int(NREP); idx += int(blockDim.x)) {
     const uint32_t z = uint32_t(idx) / NREP;
-    uint32_t mk = 0, mv = 0;
-    for (int m = 1; m < a.Mk; ++m) mk = (z >= a.ck[m]) ? uint32_t(m) : mk;
-    for (int m = 1; m < a.Mv; ++m) mv = (z >= a.cv[m]) ? uint32_t(m) : mv;
-    const uint32_t ek = a.fk[mk] | ((z - a.ck[mk]) << 8) | (a.lvk[mk] << 16);
-    const uint32_t ev = a.fv[mv] | ((z - a.cv[mv]) << 8) | (mv << 16);
+    const uint32_t ek = a.tabk[z], ev = a.tabv[z];
     if (PERM) {
       const uint32_t row = Lay::P_TAB + z * 256u + (uint32_t(idx) % NREP) * 4u;
       *reinterpret_cast<uint32_t*>(lds + row) = ek;

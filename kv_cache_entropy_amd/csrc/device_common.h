@@ -112,6 +112,10 @@ struct Attn2Args {
   uint32_t lvk[kMaxLevels];   // fp16 bits of the key levels
   uint32_t lbv[kMaxLevels];   // low bytes of the fp16 value levels (0 when affine)
   int v_lo_nonzero;           // some value level has a nonzero low byte
+  // decode-table entries of the fused kernels, slot z = state mod 256: f | (z - c) << 8
+  // in the low half; the high half holds the fp16 bits of the key level (K) or
+  // the level index (V)
+  uint32_t tabk[256], tabv[256];
 };
 
 // The uncompressed tail of every sequence (the most recent tokens, kept in
