@@ -1194,17 +1194,31 @@ __device__ __forceinline__ void pair_post(uint32_t* counter, uint32_t value, int
 template <int NGM>
 __device__ inline void pv_half_int(const uint8_t* vch, int lane, int qn, const uint16_t* wv, const uint16_t* wv_lo,
                                    uint32_t lutHi, uint32_t lutLo, float4_t (&O)[NGM]) {
-#pragma unroll 2
-  for (int tq = 0; tq < 16; ++tq) {
-    const uint32_t idx = *reinterpret_cast<const uint32_t*>(vch + lane * kChunk8Stride + 4 * tq);
-    const uint32_t hb = __builtin_amdgcn_perm(lutHi, lutLo, idx);
-    const half4_t B = as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu), __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
+  // 4 columns per batch: every LDS load of the batch first, then the
+  // lookups and products
 #pragma unroll
-    for (int m = 0; m < NGM; ++m) {
-      const uint2 ah = *reinterpret_cast<const uint2*>(wv + (m * 4 + qn) * 64 + 4 * tq);
-      const uint2 al = *reinterpret_cast<const uint2*>(wv_lo + (m * 4 + qn) * 64 + 4 * tq);
-      O[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah.x, ah.y), B, O[m], 0, 0, 0);
-      O[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al.x, al.y), B, O[m], 0, 0, 0);
+  for (int t0 = 0; t0 < 16; t0 += 4) {
+    uint32_t idx[4];
+    uint2 ah[4][NGM], al[4][NGM];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      idx[u] = *reinterpret_cast<const uint32_t*>(vch + lane * kChunk8Stride + 4 * (t0 + u));
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) {
+        ah[u][m] = *reinterpret_cast<const uint2*>(wv + (m * 4 + qn) * 64 + 4 * (t0 + u));
+        al[u][m] = *reinterpret_cast<const uint2*>(wv_lo + (m * 4 + qn) * 64 + 4 * (t0 + u));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t hb = __builtin_amdgcn_perm(lutHi, lutLo, idx[u]);
+      const half4_t B =
+          as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu), __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
+#pragma unroll
+      for (int m = 0; m < NGM; ++m) {
+        O[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(ah[u][m].x, ah[u][m].y), B, O[m], 0, 0, 0);
+        O[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(as_half4(al[u][m].x, al[u][m].y), B, O[m], 0, 0, 0);
+      }
     }
   }
 }
