@@ -1487,6 +1487,11 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   const uint32_t lutHi2 = a.lbv[4] | (a.lbv[5] << 8) | (a.lbv[6] << 16) | (a.lbv[7] << 24);
   asm volatile("" : "+v"(lutLo), "+v"(lutHi));
   const bool lo_levels = a.v_lo_nonzero != 0;
+  // A workgroup of at most 4 pairs leaves pairs 4..7's areas unused: there
+  // the V wave keeps the second half of a step in pair pw + 4's VCH area and
+  // decodes a whole step before it needs the step's weights.
+  constexpr uint32_t kVch2 = uint32_t(kPairs / 2) * (PERM ? Lay::P_SIZE : Lay::SIZE);
+  const bool two_vch = blockDim.x <= 128u * (kPairs / 2);
   // Output accumulators, rotated once per step so that V's head is O[0]; after
   // NT HKV steps O[j] holds KV head j again.
   float4_t O[HKV][2][NGM];
@@ -1566,8 +1571,27 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
       if (g == 0) xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
       const uint16_t* const wv = wts;
       const uint16_t* const wv_lo = wv + NW * 64;
+      auto rescale = [&]() {
+        if (alv[15] != 0.f) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int m = 0; m < NGM; ++m)
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) O[0][c][m][ii] *= alv[m * 4 + ii];
+        }
+      };
+      auto pv = [&](const uint8_t* vc, int ch) {
+        wave_lds_fence();
+        if (lo_levels)
+          pv_half<NGM, true>(vc, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[0][ch]);
+        else
+          pv_half_int<NGM>(vc, lane, qn, wv, wv_lo, lutHi, lutLo, O[0][ch]);
+        wave_lds_fence();
+      };
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
+        uint8_t* const vc = vch + (ch == 1 && two_vch ? kVch2 : 0u);
 #pragma unroll 1
         for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
@@ -1582,28 +1606,26 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const uint32_t ev = dec5_step<PERM, Lay::SLOT_SHIFT, TAB>(xv, winV, selv, lds, toffV);
-                vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
+                vc[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
               }
               rv.P += selv - kSel0;
             }
           }
-        if (ch == 0) {
-          pair_wait(ready, step + 1u);                  // the K wave's weights of (i, g)
-          if (alv[15] != 0.f) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-              for (int m = 0; m < NGM; ++m)
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) O[0][c][m][ii] *= alv[m * 4 + ii];
+        if (two_vch) {
+          // both halves decoded before the step's weights are needed
+          if (ch == 1) {
+            pair_wait(ready, step + 1u);                // the K wave's weights of (i, g)
+            rescale();
+            pv(vch, 0);
+            pv(vch + kVch2, 1);
           }
+        } else {
+          if (ch == 0) {
+            pair_wait(ready, step + 1u);                // the K wave's weights of (i, g)
+            rescale();
+          }
+          pv(vch, ch);
         }
-        wave_lds_fence();
-        if (lo_levels)
-          pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[0][ch]);
-        else
-          pv_half_int<NGM>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, O[0][ch]);
-        wave_lds_fence();
       }
       pair_post(done, ++step, lane);
       // rotate: the next step's head becomes O[0]
