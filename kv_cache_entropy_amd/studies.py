@@ -10,8 +10,11 @@ Analogues, on seeded synthetic KV, of the measurements of the page
     (2.68 / 1.84 bits per value);
   * §5.4 Figure 4 (middle, right): error against the storage budget at 8/6
     levels, and against the K/V split of a fixed 2.26-bit budget;
-  * Appendix C: changed-symbol fractions after drift and the extra rate of the
-    analytic model against the measured symbol distributions.
+  * Appendix C, Figure 6: the largest feasible alphabet against the payload,
+    beside equal-rate fixed-width coding (left); the measured symbol
+    distributions against the analytic model and the coding table (middle);
+    the distribution of the container budget left after drift, and the
+    fractions of symbols drift changed (right).
 Containers are written and read by libkvq (the same kernels the tests check
 bit-exactly against the oracle); torch only measures errors and histograms.
 The inputs are the Llama-shaped GQA workload's distribution (per-channel key
@@ -154,6 +157,91 @@ def run_config(sm, mk, mv, ck, cv, attention=True, values=(None, None)):
     return out
 
 
+RATE_ONE = 1 << 16          # the plan's rates r_fx are bits in this fixed point
+STATE_BITS = 32             # sigma: the final rANS state at the head of a container
+
+
+def budget_fx(container_bytes):
+    """B = 8 C - sigma bits ([D-Quant] §4.2 Eq. (3)) in the rates' fixed point."""
+    return (8 * int(container_bytes) - STATE_BITS) * RATE_ONE
+
+
+def max_alphabet(n_kv_heads, head_dim, payload_bits, alpha=1.4, max_levels=16):
+    """Figure 6 (left) analogue.  For each payload b (bits per value), the
+    container C = ceil((b n + sigma) / 8) bytes, its actual payload
+    b' = (8 C - sigma) / n, and the largest alphabet M (2..max_levels) whose
+    plan is feasible: every value of a stream fits at the cheapest level,
+    n r_min <= B (the criterion of Table 2's dashes).  Fixed-width coding at
+    the same rate holds M <= 2^b' levels when charged the ideal log2 M bits
+    per symbol (as in Appendix B) and 2^floor(b') at whole bits per symbol.
+    Returns rows {payload_bits, container_bytes, feasible: [M...], ...}."""
+    n = n_kv_heads * head_dim
+    rows = []
+    for b in payload_bits:
+        C = int(math.ceil((b * n + STATE_BITS) / 8))
+        bb = (8 * C - STATE_BITS) / n
+        feasible = []
+        for M in range(2, max_levels + 1):
+            try:
+                # the key side decides; the value side gets room to spare
+                kvq.Plan(n_kv_heads, head_dim, M, 2, C, 8192, 128, alpha)
+                feasible.append(M)
+            except kvq.KvqError as e:
+                if e.status != -2:
+                    raise
+        rows.append({"payload_bits": b, "container_bytes": C, "actual_payload_bits": round(bb, 6),
+                     "feasible_levels": feasible, "max_levels_entropy": max(feasible) if feasible else None,
+                     "max_levels_fixed_width_ideal": int(math.floor(2.0 ** bb + 1e-9)),
+                     "max_levels_fixed_width_whole_bits": 1 << int(math.floor(bb + 1e-9))})
+    return rows
+
+
+def drift_study(plan, k, v, edges_bits=(0, 8, 16, 32, 64, 128, 256, 512, 1024, 4096)):
+    """Figure 6 (right) analogue on the GPU path: encodes k, v [S, T, n] with
+    the plan and returns, per side, the symbol counts, the number of symbols
+    drift changed (against nearest rounding on the final grid, the encoder's
+    counters), and every stream's remaining budget B - sum_i r(m_i) in the
+    rates' fixed point (the quantity drift keeps non-negative, Eq. (6)), with
+    a histogram over edges_bits (bits)."""
+    S, T = int(k.shape[0]), int(k.shape[1])
+    c = kvq.alloc_cache(plan, S, T)
+    stats = torch.zeros(8, dtype=torch.int64, device="cuda")
+    kvq.kvq_encode_streams(plan, k, v, c["k_cont"], c["v_cont"], c["k_so"], c["v_so"],
+                           c["k_mean_q"], c["k_mean_scale"], stats=stats)
+    st = stats.cpu().tolist()
+    out = {"streams_per_side": S * T, "values_per_stream": plan.n,
+           "containers": [plan.params.container_bytes_k, plan.params.container_bytes_v],
+           "levels": [plan.params.levels_k, plan.params.levels_v]}
+    for side, key, name in ((0, "k_cont", "k"), (1, "v_cont", "v")):
+        sym = torch.empty(S, T, plan.n, dtype=torch.uint8, device="cuda")
+        kvq.kvq_decode_symbols(plan, side, c[key], sym)
+        f, _, r = plan.tables(side)
+        M = len(f)
+        rate = torch.tensor(r, dtype=torch.int64, device="cuda")
+        used = rate[sym.long()].sum(dim=-1).flatten()
+        C = out["containers"][side]
+        rem = (budget_fx(C) - used).cpu()
+        counts = torch.bincount(sym.flatten().long(), minlength=M).cpu().tolist()
+        rem_bits = rem.double() / RATE_ONE
+        e = torch.tensor(list(edges_bits), dtype=torch.float64)
+        hist = [int(((rem_bits >= e[i]) & (rem_bits < e[i + 1])).sum()) for i in range(len(e) - 1)]
+        changed = st[2] if side == 0 else st[6]
+        out[name] = {
+            "symbol_counts": counts,
+            "changed_symbols": int(changed),
+            "changed_frac": changed / (S * T * plan.n),
+            "fallbacks": int(st[0] + st[1]) if side == 0 else int(st[4] + st[5]),
+            "overruns": int(st[3] if side == 0 else st[7]),
+            "remaining_fx": [int(x) for x in rem.tolist()],
+            "remaining_bits": {"min": float(rem_bits.min()), "median": float(rem_bits.median()),
+                               "mean": float(rem_bits.mean()), "max": float(rem_bits.max()),
+                               "below_8_bits_frac": float((rem_bits < 8).double().mean())},
+            "remaining_hist": {"edges_bits": list(edges_bits), "counts": hist},
+        }
+    torch.cuda.synchronize()
+    return out
+
+
 def unpack_fw(cont, levels, n):
     """Symbols of fixed-width containers (the layout of kvq_encode_fixed_width)."""
     b = 1
@@ -206,7 +294,9 @@ def main(argv=None):
     if not torch.cuda.is_available():
         sys.exit("the studies run the HIP library and need a GPU")
     sm = Sample(args.seqs, args.tokens)
-    res = {"sample": f"gqa distribution, sequences 0..{args.seqs - 1}, {args.tokens} tokens each"}
+    res = {"sample": f"gqa distribution, sequences 0..{args.seqs - 1}, {args.tokens} tokens each",
+           "command": "python -m kv_cache_entropy_amd.studies " + " ".join(sys.argv[1:] if argv is None else argv),
+           "device": torch.cuda.get_device_name(0)}
     print(f"# Synthetic studies ({res['sample']})\n")
 
     # Table 1 analogue: 8 levels, a container large enough that drift never acts
@@ -272,6 +362,43 @@ def main(argv=None):
           f"coding table: K {d['table_gap_k']:.4f}, V {d['table_gap_v']:.4f}")
     print(f"* measured K histogram {d['hist_k']}")
     print(f"* measured V histogram {d['hist_v']}")
+    # Figure 6 analogues
+    w = sm.w
+    pay = [0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.25, 2.5, 2.75, 3.0, 3.5, 4.0]
+    left = max_alphabet(w.n_kv_heads, w.head_dim, pay)
+    res["figure6_left"] = left
+    print("\n## Largest feasible alphabet against the payload (Figure 6 left analogue)\n")
+    print("Feasible: every value of a stream fits at the cheapest level (n r_min <= 8C - 32 bits).\n")
+    print("| payload bits/value | container bytes | entropy-coded max levels | fixed width, ideal log2 M | "
+          "fixed width, whole bits |")
+    print("|---:|---:|---:|---:|---:|")
+    for r in left:
+        print(f"| {r['actual_payload_bits']:.3f} | {r['container_bytes']} | {r['max_levels_entropy']} | "
+              f"{r['max_levels_fixed_width_ideal']} | {r['max_levels_fixed_width_whole_bits']} |")
+    res["figure6_right"] = []
+    print("\n## Container budget left after drift (Figure 6 right analogue)\n")
+    for ck, cv in ((331, 231), (292, 203)):
+        plan = kvq.Plan(w.n_kv_heads, w.head_dim, 8, 6, ck, cv, 128, 1.4)
+        ds = drift_study(plan, sm.k, sm.v)
+        slim = {key: val for key, val in ds.items() if key not in ("k", "v")}
+        for side in ("k", "v"):
+            slim[side] = {key: val for key, val in ds[side].items() if key != "remaining_fx"}
+        res["figure6_right"].append(slim)
+        edges = ds["k"]["remaining_hist"]["edges_bits"]
+        print(f"### {ck}/{cv} B, 8/6 levels ({plan.bits_per_elem(True):.3f} bits/value)\n")
+        print("| remaining bits | " + " | ".join(f"[{edges[i]}, {edges[i + 1]})" for i in range(len(edges) - 1)) + " |")
+        print("|---|" + "---:|" * (len(edges) - 1))
+        for side in ("k", "v"):
+            h = ds[side]["remaining_hist"]["counts"]
+            tot = sum(h)
+            print(f"| {side.upper()} streams | " + " | ".join(f"{x / tot:.1%}" for x in h) + " |")
+        for side in ("k", "v"):
+            d_ = ds[side]
+            rb = d_["remaining_bits"]
+            print(f"* {side.upper()}: changed symbols {d_['changed_frac']:.3%}, fallbacks {d_['fallbacks']}, "
+                  f"remaining bits min {rb['min']:.2f} / median {rb['median']:.1f} / mean {rb['mean']:.1f}, "
+                  f"streams with under 8 bits left {rb['below_8_bits_frac']:.1%}")
+        print()
     # Appendix B analogue: the fixed-width comparator at 6/3 levels
     fw = run_fixed_width(sm)
     res["fixed_width"] = fw
