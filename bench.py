@@ -69,14 +69,12 @@ def measured_traffic(workload_key, bytes_hint):
 
 def kernel_name(w, levels_v=6):
     """The fused kernel the library launches for this head layout (its dispatch
-    rule: K and V in separate waves up to 4 query heads per KV head, or 8 on at
-    most 2 KV heads; otherwise one wave with both decode chains)."""
+    rule: K and V decoded in separate waves for V alphabets of up to 8 levels;
+    a single-wave kernel otherwise)."""
     G = w.n_q_heads // w.n_kv_heads
     if levels_v > 8:
         return f"attention2_kernel<{G}, {w.n_kv_heads}>"
-    if G <= 4 or w.n_kv_heads <= 2:
-        return f"attention5_kernel<{G}, {w.n_kv_heads}>"
-    return f"attention4_kernel<{G}, {w.n_kv_heads}>"
+    return f"attention5_kernel<{G}, {w.n_kv_heads}>"
 
 
 def run_config(torch, kvq, synth, w, bi, args, dev, extras=False, cpu_sample=False):
