@@ -6,8 +6,8 @@
 // let the contractions run on the raw levels with the affine terms applied
 // afterwards.
 //
-// Two kernels share the same per-wave schedule: one wave handles a token range
-// of one sequence in 64-token tiles, lane t <-> token t0 + t.
+// The kernels handle a token range of one sequence in 64-token tiles, lane
+// t <-> token t0 + t:
 //   * QK^T: every 4 decoded K levels of a lane form the B operand of a
 //     v_mfma_f32_4x4x4f16 block (16 blocks of 4 tokens); the A operand is the
 //     rotated query of 4 heads, split into fp16 hi + lo parts after a
@@ -17,9 +17,9 @@
 //     softmax weights (hi + lo) as A.
 //   * Online softmax per query head across tiles; the per-token scale folds
 //     into the weights and the per-token offset into a separate sum (Eq. 9).
-// attention4_kernel (V alphabets of up to 8 levels) runs eight such waves per
-// workgroup with two decode chains per lane, bank-confined LDS rings and
-// replicated decode tables; its layout is described above its definition.
+// attention5_kernel (V alphabets of up to 8 levels) decodes K and V in the two
+// waves of a pair, eight pairs per workgroup sharing replicated decode tables
+// in LDS; its layout is described above its definition.
 // attention2_kernel is the single-wave form for 9-level V alphabets: 8-byte
 // decode-table entries (lo = f | fp16 level high byte << 24, hi = z - c, one
 // v_mad_u32_u24 per symbol), a 64-byte ring per lane refilled by 16-byte loads
@@ -503,77 +503,19 @@ __global__ __launch_bounds__(64, 2) void attention2_kernel(Attn2Args a) {
 }
 
 
-// ------------------------------------------- attention, eight waves per workgroup
-// Same per-wave schedule as a single-wave workgroup on one token range, with
-// two decode chains per lane: while the K stream of (tile i, KV head g) is
-// decoded and contracted with the query, the V stream of the head before it
-// in (tile, head) order is decoded into the int8 transpose chunk and
-// contracted with that head's softmax weights.  The first iteration's V work
-// and the last iteration's K work are dummies on valid containers (zero
-// weights, discarded logits).
-//
-// Eight such waves share one workgroup so that they can share decode tables
-// replicated across LDS banks.  LDS map (byte offsets, in this order):
-//   per wave (below 64 KiB, so chunk offsets fold into instructions): V chunk,
-//                softmax weights, running softmax state, the tile's per-head
-//                affine terms
-//   rings        wave w, stream s (K 0, V 1): 17 rows of 64 dwords at
-//                + (2w + s) * 4352; lane l owns dword l of every row
-//   K, V decode tables, R replicas each (R = 16, or 8 when LDS is short)
+// ------------------------------------------- LDS rings and decode tables
 // Decode-table entries are 32-bit: f | (z - c) << 8 | payload, the payload
-// being the fp16 high byte of the level in bits 24..31 (K; levels 0..8 have a
-// zero low byte) or the level index in bits 16..23 (V).  Replica r of slot z
-// is dword z*R + r, so it only occupies banks congruent to r mod R (32 banks
-// of 4 bytes); lane l reads replica l mod R.
+// being the fp16 bits of the level (K) or the level index (V) in bits
+// 16..31.  Replicated tables put replica r of a slot at a bank of its own, and
+// lane l reads replica l mod R.
 // A lane's ring holds container bytes [16 rows of 4]: frame byte p sits in
-// row (p / 4) mod 16, byte p mod 4 of the lane's dword, i.e. always in bank
-// l mod 32, so ring reads and writes never conflict.  Row 16 repeats row 0 so
-// that two consecutive rows can be read with one ds_read2.  The decoder reads
-// the 8-byte window holding the next 4 bytes once per 4 symbols and takes its
-// bytes with v_perm.
+// row (p / 4) mod 16, byte p mod 4 of the lane's own dword of that row, so the
+// lanes of a wave never share a bank in ring reads and writes.  Row 16 repeats
+// row 0 so that two consecutive rows can be read with one ds_read2.  The
+// decoder reads the 8-byte window holding the next 4 bytes once per 4 symbols
+// and takes its bytes with v_perm.
 constexpr int kChunk8Stride = 68;     // bytes per channel row of the int8 V chunk
-constexpr int kWaves = 8;
 constexpr uint32_t kRingBytes = 17u * 256u;
-
-template <int G, int HKV>
-struct Lay4 {
-  static constexpr int HQ = G * HKV;
-  static constexpr int NW = ((G + 3) / 4) * 4;
-  // per wave, at w * SIZE
-  static constexpr uint32_t VCH = 0;                                // [64 ch][68] int8 levels
-  static constexpr uint32_t WTS = 64u * kChunk8Stride;              // [hi/lo][NW][64] fp16
-  static constexpr uint32_t RUN = WTS + 2u * NW * 64u * 2u;         // 6 x [HQ] f32
-  static constexpr uint32_t SIZE = (RUN + 6u * HQ * 4u + 15u) & ~15u;
-  static constexpr uint32_t RINGS = (kWaves * SIZE + 255u) & ~255u;
-  static constexpr uint32_t RING_END = RINGS + 2u * kWaves * kRingBytes;
-  static constexpr uint32_t REPS = RING_END + 2u * 256u * 16u * 4u <= 163840u ? 16u : 8u;
-  static constexpr uint32_t TAB_BYTES = 256u * REPS * 4u;
-  static constexpr uint32_t TABK = (RING_END + TAB_BYTES - 1u) / TAB_BYTES * TAB_BYTES;
-  static constexpr uint32_t TABV = TABK + TAB_BYTES;
-  static constexpr uint32_t TOTAL = TABV + TAB_BYTES;
-  static constexpr uint32_t SLOT_SHIFT = REPS == 16u ? 6u : 5u;     // log2(REPS * 4)
-  static_assert(kWaves * SIZE <= 65536u, "per-wave regions must sit below 64 KiB");
-  static_assert(TOTAL <= 163840u, "exceeds the LDS of a CU");
-
-  // Interleaved layout, used when it fits (PERM): decode-table slot z is row z
-  // (256 bytes) of a 64 KiB region at P_TAB - K replica r at byte 4 r, V
-  // replica r at byte 64 + 4 r - so the address of a lookup is one v_perm that
-  // puts the state's low byte in byte 1 of the lane's replica offset.  Bytes
-  // 128..255 of every row hold ring rows.  Rings then have a row pitch of 512
-  // bytes: lanes 0..31 in the upper half of one table row, lanes 32..63 in the
-  // next one (or, outside the table region, two rings share 512-byte rows,
-  // one at byte 0 and one at byte 128 of each half).  A lane keeps one bank.
-  static constexpr uint32_t P_TAB = (kWaves * SIZE + 255u) & ~255u;
-  static constexpr uint32_t P_RING_BYTES = 17u * 512u;
-  static constexpr int P_RINGS_IN_TAB = 7;                   // 7 x 17 of the 128 row pairs
-  static constexpr uint32_t P_RINGS = P_TAB + 65536u;
-  static constexpr int P_PAIRS = (2 * kWaves - P_RINGS_IN_TAB + 1) / 2;
-  static constexpr uint32_t P_TOTAL = P_RINGS + uint32_t(P_PAIRS) * P_RING_BYTES;
-  static constexpr bool PERM = P_TOTAL <= 163840u && P_TAB <= 65535u;
-  static constexpr uint32_t LDS_BYTES = PERM ? P_TOTAL : TOTAL;
-  static constexpr int RS = PERM ? 9 : 8;                    // log2 of the ring row pitch
-  static_assert(uint32_t(P_RINGS_IN_TAB) * P_RING_BYTES <= 65536u, "rings overflow the table region");
-};
 
 __device__ inline void wave_lds_fence() {
   // LDS instructions of one wave execute in order; this only keeps the
@@ -754,362 +696,27 @@ __device__ inline void pv_half(const uint8_t* vch, int lane, int qn, const uint1
   }
 }
 
-template <int G, int HKV>
-__global__ __launch_bounds__(64 * kWaves, 1) void attention4_kernel(Attn2Args a, int64_t S) {
-  using Lay = Lay4<G, HKV>;
-  constexpr int HQ = Lay::HQ;
-  constexpr int NGM = (G + 3) / 4;
-  constexpr int NW = Lay::NW;
-  constexpr bool PERM = Lay::PERM;
-  constexpr int RS = Lay::RS;
-  __shared__ __align__(16) uint8_t lds[Lay::LDS_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  // decode tables, shared by the workgroup (PERM: 16 replicas per table in
-  // each 256-byte row; otherwise REPS contiguous replicas per slot)
-  // Decode tables: entry idx of the replicated table is the host's entry for
-  // slot idx / NREP (one load from the kernel arguments).
-  constexpr uint32_t NREP = PERM ? 16u : Lay::REPS;
-#pragma unroll 4
-  for (int idx = tid; idx < 256 * int(NREP); idx += int(blockDim.x)) {
-    const uint32_t z = uint32_t(idx) / NREP;
-    const uint32_t ek = a.tabk[z], ev = a.tabv[z];
-    if (PERM) {
-      const uint32_t row = Lay::P_TAB + z * 256u + (uint32_t(idx) % NREP) * 4u;
-      *reinterpret_cast<uint32_t*>(lds + row) = ek;
-      *reinterpret_cast<uint32_t*>(lds + row + 64u) = ev;
-    } else {
-      reinterpret_cast<uint32_t*>(lds + Lay::TABK)[idx] = ek;
-      reinterpret_cast<uint32_t*>(lds + Lay::TABV)[idx] = ev;
-    }
-  }
-  __syncthreads();
-
-  // a workgroup has up to kWaves waves (fewer when the launch is small, to
-  // spread it over more CUs); wave w of workgroup b owns split-wave b * wpw + w
-  const int64_t gw = int64_t(blockIdx.x) * (blockDim.x >> 6) + w;
-  if (gw >= S * a.nsplit) return;          // (no workgroup barrier follows)
-  const int64_t s = gw / a.nsplit;
-  const int split = int(gw - s * a.nsplit);
-
-  uint8_t* const mine = lds + uint32_t(w) * Lay::SIZE;
-  uint8_t* const vch = mine + Lay::VCH;
-  uint16_t* const wts = reinterpret_cast<uint16_t*>(mine + Lay::WTS);    // [hi/lo][NW][64]
-  float* const runM = reinterpret_cast<float*>(mine + Lay::RUN);
-  float* const runL = runM + HQ;
-  float* const runZ = runL + HQ;
-  float* const affS = runZ + HQ;
-  float* const affQ = affS + HQ;
-  float* const affM = affQ + HQ;
-  for (int h = lane; h < HQ; h += 64) {
-    runM[h] = -__builtin_inff();
-    runL[h] = 0.f;
-    runZ[h] = 0.f;
-  }
-  for (int i = lane; i < 2 * NW * 64; i += 64) wts[i] = 0;
-
-  // lane l < 2G feeds the running sum of value sum_k bit_k(l) (2G >> (k + 1)):
-  // query head (that value) / 2, sum of p (even) or of p o (odd)
-  float* sum_slot = runL;
-  {
-    int idx = 0;
-#pragma unroll
-    for (int b = 0, w2 = G; w2 >= 1; ++b, w2 >>= 1) idx += ((lane >> b) & 1) * w2;
-    sum_slot = ((idx & 1) ? runZ : runL) + (idx >> 1);
-  }
-  uint32_t toffK, toffV;
-  Ring5 rk, rv;
-  if (PERM) {
-    toffK = opaque(uint32_t(lane % 16) * 4u);
-    toffV = opaque(64u + uint32_t(lane % 16) * 4u);
-    // ring i = 2 w + stream: the first P_RINGS_IN_TAB in the table rows' upper
-    // halves, the others in pairs after the table region
-    const uint32_t lane_off = uint32_t(lane >> 5) * 256u + uint32_t(lane & 31) * 4u;
-    auto ring_off = [&](int i) -> uint32_t {
-      if (i < Lay::P_RINGS_IN_TAB) return Lay::P_TAB + uint32_t(i) * Lay::P_RING_BYTES + 128u + lane_off;
-      const int j = i - Lay::P_RINGS_IN_TAB;
-      return Lay::P_RINGS + uint32_t(j / 2) * Lay::P_RING_BYTES + uint32_t(j % 2) * 128u + lane_off;
-    };
-    rk.off = opaque(ring_off(2 * w));
-    rv.off = opaque(ring_off(2 * w + 1));
-  } else {
-    toffK = opaque(Lay::TABK + uint32_t(lane % Lay::REPS) * 4u);
-    toffV = opaque(Lay::TABV + uint32_t(lane % Lay::REPS) * 4u);
-    rk.off = opaque(Lay::RINGS + uint32_t(2 * w) * kRingBytes + uint32_t(lane) * 4u);
-    rv.off = opaque(Lay::RINGS + uint32_t(2 * w + 1) * kRingBytes + uint32_t(lane) * 4u);
-  }
-  wave_lds_fence();
-
-  // fp16 high bytes of V levels 0..7 as a v_perm lookup (low byte is zero)
-  const uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
-  const uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
-  // low bytes of non-integer value levels (all zero for integer levels)
-  const uint32_t lutLo2 = a.lbv[0] | (a.lbv[1] << 8) | (a.lbv[2] << 16) | (a.lbv[3] << 24);
-  const uint32_t lutHi2 = a.lbv[4] | (a.lbv[5] << 8) | (a.lbv[6] << 16) | (a.lbv[7] << 24);
-
-  // Output accumulators, rotated once per head step so that the loop over
-  // heads needs no register indexing: at the start of step g, O[j] holds KV
-  // head (g - 1 + j) mod HKV, so V's head is O[0] and K's head is O[KJ].
-  constexpr int KJ = 1 % HKV;
-  float4_t O[HKV][2][NGM];
-#pragma unroll
-  for (int g = 0; g < HKV; ++g)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int m = 0; m < NGM; ++m) O[g][c][m] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t tb = int64_t(split) * a.tokens_per_split;
-  const int64_t te = tb + a.tokens_per_split < a.T ? tb + a.tokens_per_split : a.T;
-  const int64_t NT = (te - tb) / 64;
-  const uint4* qop = a.qop + s * (HKV * NGM * 32 * 4);
-  const float* qscale = a.qscale + s * HQ;
-  const float* qsum = a.qsum + s * HQ;
-  const float* qmu = a.qmu + s * HQ * a.nW;
-  const int qn = lane & 3;
-  // The query operand of channel quad c = 16 ch + 8 t + j (ch, t in {0, 1},
-  // j < 8) is held by the lanes of MFMA block 8 ch + j, in register t: each
-  // QK^T MFMA broadcasts that block's A operand to all 16 blocks (CBSZ = 4,
-  // ABID = 8 ch + j), so one head's query takes two registers per lane and
-  // is loaded once per head, a head ahead, not once per channel quad.
-  // (With two MFMA groups of query heads the prefetch would not fit the
-  // register file; the head's query is then loaded at the head's start.)
-  const int qc0 = 16 * ((lane >> 2) >> 3) + ((lane >> 2) & 7);
-  constexpr bool kQPrefetch = NGM == 1;
-  uint4 qnx[NGM][2];
-#pragma unroll
-  for (int m = 0; m < NGM; ++m)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) qnx[m][t] = kQPrefetch ? qop[(m * 32 + qc0 + 8 * t) * 4 + qn] : uint4{};
-  const uint16_t* const wv = wts;                 // weights of the head whose V is decoded
-  const uint16_t* const wv_lo = wts + NW * 64;
-
-  uint32_t xk = 0, xv = 0;
-  float sk = 0.f, ok = 0.f, svK = 0.f, ovK = 0.f;
-  // buffer resources over this sequence's containers (T C < 2^31, checked by the host)
-  const uint8_t* const kseq = a.k_cont + s * a.T_cap * a.CK;
-  const uint8_t* const vseq = a.v_cont + s * a.T_cap * a.CV;
-  const __amdgpu_buffer_rsrc_t rsK = seq_rsrc(kseq, uint32_t(a.T * a.CK));
-  const __amdgpu_buffer_rsrc_t rsV = seq_rsrc(vseq, uint32_t(a.T * a.CV));
-  const uint32_t misK = uint32_t(reinterpret_cast<uintptr_t>(kseq) & 15u);
-  const uint32_t misV = uint32_t(reinterpret_cast<uintptr_t>(vseq) & 15u);
-
-  for (int64_t i = 0; i <= NT; ++i) {
-    const bool kreal = i < NT;
-    const int64_t tK = tb + 64 * (kreal ? i : NT - 1);        // K tile (clamped dummy)
-#pragma unroll 1
-    for (int g = 0; g < HKV; ++g) {
-      if (!kreal && g > 0) break;
-      // ---- stream starts
-      if (g == 0) {
-        const int64_t row = s * a.T_cap + tK + lane;
-        xk = ring5_start<RS>(rk, lds, rsK, misK + uint32_t(tK + lane) * uint32_t(a.CK), uint32_t(a.CK));
-        sk = h2f(a.k_so[2 * row]);
-        ok = h2f(a.k_so[2 * row + 1]);
-        svK = h2f(a.v_so[2 * row]);
-        ovK = h2f(a.v_so[2 * row + 1]);
-        const int64_t wdx = tK >> a.log2W;
-        // logits are kept in log2 units: tau log2(e) folds into the affine terms
-        const float tl = a.tau * 1.4426950408889634f;
-        for (int h = lane; h < HQ; h += 64) {
-          affS[h] = tl * qscale[h];
-          affQ[h] = tl * qsum[h];
-          affM[h] = tl * qmu[h * a.nW + wdx];
-        }
-        wave_lds_fence();
-      }
-      const int vg = (g + HKV - 1) % HKV;                      // V's KV head this iteration
-      if (vg == 0 || (i == 0 && g == 0)) {                     // V starts a container
-        // (the very first iteration always starts one: its V work is the
-        // dummy on tile 0, and the ring must point at valid memory)
-        const int64_t vt = (g == 0) ? i - 1 : i;               // V's tile (-1: dummy on tile 0)
-        const int64_t tV = tb + 64 * (vt < 0 ? 0 : (vt >= NT ? NT - 1 : vt));
-        xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
-      }
-
-      float4_t D[NGM];
-#pragma unroll
-      for (int m = 0; m < NGM; ++m) D[m] = float4_t{0.f, 0.f, 0.f, 0.f};
-      uint4 qh[NGM][2];
-      {
-        const int gn = kQPrefetch ? (g + 1 < HKV ? g + 1 : 0) : g;    // the head whose query is loaded
-        const uint4* qg = qop + gn * (NGM * 32 * 4) + qn;
-#pragma unroll
-        for (int m = 0; m < NGM; ++m)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            if (kQPrefetch) {
-              qh[m][t] = qnx[m][t];
-              qnx[m][t] = qg[(m * 32 + qc0 + 8 * t) * 4];
-            } else {
-              qh[m][t] = qg[(m * 32 + qc0 + 8 * t) * 4];
-            }
-          }
-      }
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-#pragma unroll 1
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int bh = 0; bh < 2; ++bh) {
-          // two blocks per trip, one per refill slot: each slot's chunk stays
-          // in the same registers across the loop's back edge
-          const int b4 = 2 * b2 + bh;
-          if (bh == 1) {
-            ring5_block<1, RS>(rk, lds, rsK);
-            ring5_block<1, RS>(rv, lds, rsV);
-          } else {
-            ring5_block<0, RS>(rk, lds, rsK);
-            ring5_block<0, RS>(rv, lds, rsV);
-          }
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            uint32_t e[4];
-            const uint32_t winK = ring5_window<RS>(rk, lds), winV = ring5_window<RS>(rv, lds);
-            uint32_t selk = kSel0, selv = kSel0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              e[r] = dec5_step<PERM, Lay::SLOT_SHIFT, Lay::P_TAB>(xk, winK, selk, lds, toffK);
-              const uint32_t ev = dec5_step<PERM, Lay::SLOT_SHIFT, Lay::P_TAB>(xv, winV, selv, lds, toffV);
-              vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
-            }
-            rk.P += selk - kSel0;
-            rv.P += selv - kSel0;
-            const half4_t B = as_half4(__builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
-                                       __builtin_amdgcn_perm(e[3], e[2], 0x07060302u));
-#pragma unroll
-            for (int m = 0; m < NGM; ++m) {
-              D[m] = mfma_bcast_a(as_half4(qh[m][0].x, qh[m][0].y), B, D[m], 8 * ch + 4 * bh + cc);
-              D[m] = mfma_bcast_a(as_half4(qh[m][0].z, qh[m][0].w), B, D[m], 8 * ch + 4 * bh + cc);
-            }
-          }
-          if (bh == 1) {
-            // the trip's second half is done: the other register's quads come next
-#pragma unroll
-            for (int m = 0; m < NGM; ++m) {
-              const uint4 t = qh[m][0];
-              qh[m][0] = qh[m][1];
-              qh[m][1] = t;
-            }
-          }
-        }
-        // PV of V's head for the 64 channels of this half
-        wave_lds_fence();
-        if (a.v_lo_nonzero)
-          pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[0][ch]);
-        else
-          pv_half<NGM, false>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, 0u, 0u, O[0][ch]);
-        wave_lds_fence();
-      }
-      // ---- K head g done: logits -> online softmax -> weights for the next iteration
-      if (kreal) {
-        uint16_t* const wk = wts;
-        // Lazy running maximum: while no lane's logit exceeds a head's running
-        // maximum M, the weights are taken against M as it stands (exp2 of a
-        // non-positive number, so every weight stays in (0, 1]) and nothing is
-        // rescaled; only when some logit exceeds M is the tile maximum reduced,
-        // M raised and the head's sums and accumulators rescaled.  The tile's
-        // sums of p and p o over the wave, for all G heads at once, come from
-        // one reduce-scatter, and lane 2v + z (z = 0: sum p, 1: sum p o) adds
-        // its total to the running sum of head v.
-        float sums[2 * G];
-#pragma unroll
-        for (int v = 0; v < NW; ++v) {
-          const int m = v / 4, ii = v % 4;
-          float whi = 0.f, wlo = 0.f;
-          if (v < G) {
-            const int h = g * G + v;
-            const float lg = __builtin_fmaf(sk, D[m][ii] * affS[h], __builtin_fmaf(ok, affQ[h], affM[h]));
-            float Mr = runM[h];
-            if (__builtin_amdgcn_ballot_w64(lg > Mr) != 0) {
-              const float Mn = fmaxf(Mr, wave_max_dpp(lg));
-              const float al = __builtin_amdgcn_exp2f(Mr - Mn);
-              runL[h] *= al;
-              runZ[h] *= al;
-#pragma unroll
-              for (int c = 0; c < 2; ++c) O[KJ][c][m][ii] *= al;
-              Mr = Mn;
-              runM[h] = Mn;
-            }
-            const float p = __builtin_amdgcn_exp2f(lg - Mr);
-            sums[2 * v] = p;
-            sums[2 * v + 1] = p * ovK;
-            const float wt = p * svK;
-            const __half hh = __float2half_rn(wt);
-            whi = wt;
-            wlo = wt - __half2float(hh);
-          }
-          wk[v * 64 + lane] = __half_as_ushort(__float2half_rn(whi));
-          wk[NW * 64 + v * 64 + lane] = __half_as_ushort(__float2half_rn(wlo));
-        }
-        const float tot = wave_sum_scatter<2 * G>(sums, lane);
-        if (lane < 2 * G) atomicAdd(sum_slot + g * G, tot);
-        wave_lds_fence();
-      }
-      // rotate: the next step's V head (this step's K head) becomes O[0]
-      if (HKV > 1) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int m = 0; m < NGM; ++m) {
-            const float4_t t = O[0][c][m];
-#pragma unroll
-            for (int j = 0; j + 1 < HKV; ++j) O[j][c][m] = O[j + 1][c][m];
-            O[HKV - 1][c][m] = t;
-          }
-      }
-    }
-  }
-  // The last step (i = NT, g = 0) rotated too, so O[j] now holds KV head j.
-
-  float* P = a.part + (s * a.part_splits + split) * int64_t(HQ) * (kD + 4);
-#pragma unroll
-  for (int g = 0; g < HKV; ++g)
-#pragma unroll
-    for (int m = 0; m < NGM; ++m)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int v = m * 4 + ii;
-        if (v < G) {
-          const int h = g * G + v;
-#pragma unroll
-          for (int c = 0; c < 2; ++c) P[h * (kD + 4) + c * 64 + lane] = O[g][c][m][ii];
-          if (lane == 0) {
-            P[h * (kD + 4) + kD] = runM[h] * 0.6931471805599453f;      // back to natural log units
-            P[h * (kD + 4) + kD + 1] = runL[h];
-            P[h * (kD + 4) + kD + 2] = runZ[h];
-          }
-        }
-      }
-}
-
 // -------------------------------- attention, K and V decode in separate waves
-// The same per-step work as attention4_kernel, split between the two waves of
-// a pair that share one split (token range of one sequence): the K wave
-// decodes the K stream of (tile, KV head) and contracts it with the query,
-// runs the online softmax and writes the head's weights; the V wave decodes
-// the V stream of the same (tile, head) one step later and contracts it with
-// those weights.  Each wave runs one decode chain, and a CU holds 16 waves
-// (8 pairs, 4 waves per SIMD): the SIMDs' schedulers interleave four
-// independent chains where attention4_kernel interleaves two chains in each
-// of two waves.
+// The two waves of a pair share one split (token range of one sequence): the
+// K wave decodes the K stream of (tile, KV head), contracts it with the query,
+// runs the online softmax and stores the head's weights; the V wave decodes
+// the V stream of the same (tile, head) and contracts it with those weights.
+// Each wave runs one decode chain, and a CU holds 16 waves (8 pairs, 4 waves
+// per SIMD), so each SIMD interleaves four independent chains.
 //
-// Steps are (tile, head) in order; one workgroup barrier per step: the K wave
-// passes barrier s after writing step s's weights into buffer s mod 2, the V
-// wave passes it before reading them.  Buffer s mod 2 is written again only
-// after barrier s + 1, which the V wave reaches after its step s.  Every wave
-// of the workgroup passes the same number of barriers (tokens_per_split / 64
-// times HKV): a pair whose split is shorter, or that has no split at all,
-// passes the remaining ones without work.
+// Steps are (tile, head) in order.  The waves of a pair hand steps over
+// through two LDS counters (pair_wait / pair_post), never through a
+// workgroup barrier, so pairs do not wait for one another: the K wave stores
+// step s's weights once the V wave has posted that it finished step s - 1,
+// then posts s + 1; the V wave decodes the first half of step s (with at most
+// 4 pairs per workgroup, both halves) before it waits for that post.
 //
-// LDS map: per pair (VCH: [64 ch][68] int8 V levels; WTS: 2 buffers of
-// [hi/lo][NW][64] fp16 weights; ALV: 2 buffers of the step's rescale factors
-// and a grow flag; RUN: running max, sums and the tile's affine terms), then
-// the pairs' rings (K ring 2p, V ring 2p + 1, 17 rows of 64 dwords), then the
-// K and V decode tables with REPS replicas (16, 8 or 4, the most that fit).
+// LDS map: per pair (VCH: [64 ch][68] int8 V levels of a half step; WTS: one
+// step's [hi/lo][NW][64] fp16 weights; ALV: the step's rescale factors, a grow
+// flag and the two counters; RUN: running max, sums and the tile's affine
+// terms), then the pairs' rings (K ring 2p, V ring 2p + 1, 17 rows of 64
+// dwords), then the K and V decode tables with REPS replicas (16, 8 or 4, the
+// most that fit) - or, when it fits, the interleaved layout (PERM) below.
 constexpr int kPairs = 8;
 
 template <int G, int HKV>
@@ -1927,41 +1534,25 @@ bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int 
   const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
   const bool h_ok = hkv == 1 || hkv == 2 || hkv == 4 || hkv == 8;
   if (d != kD || !g_ok || !h_ok || window < 64) return false;
-  // the eight-wave kernel takes any key levels and up to 8 value levels; the
+  // the split-wave kernel takes any key levels and up to 8 value levels; the
   // single-wave one (9 value levels) needs integer levels
   if (levels_v <= 8) return true;
   return affine && levels_k <= 9 && levels_v <= 9;
 }
 
-constexpr bool kUseSplitWaves = true;
-
 template <int G, int HKV>
 static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stream) {
-  // the interleaved kernel keeps V levels as int8 and maps them to fp16 with
-  // an 8-entry lookup, so it serves V alphabets of up to 8 levels
-  constexpr bool kSplit = kUseSplitWaves;
-  if constexpr (kSplit) {
-    if (a.Mv <= 8) {
-      // 8 query heads on more than 2 KV heads need splits of one tile
-      if (G == 8 && HKV > 2 && a.tokens_per_split != 64) return hipErrorInvalidValue;
-      const int64_t pairs = S * a.nsplit;
-      constexpr int64_t kCUs = 256;
-      int64_t ppw = (pairs + kCUs - 1) / kCUs;
-      ppw = ppw < 1 ? 1 : (ppw > kPairs ? kPairs : ppw);
-      hipLaunchKernelGGL((attention5_kernel<G, HKV>), dim3(unsigned((pairs + ppw - 1) / ppw)),
-                         dim3(unsigned(128 * ppw)), 0, stream, a, S);
-      return hipGetLastError();
-    }
-  } else if (a.Mv <= 8) {
-    const int64_t waves = S * a.nsplit;
-    // One workgroup per CU at a time (its LDS is sized for kWaves waves): a
-    // launch too small to give every CU kWaves waves uses fewer waves per
-    // workgroup and more workgroups.
+  // the split-wave kernel keeps V levels as int8 and maps them to fp16 with an
+  // 8-entry lookup, so it serves V alphabets of up to 8 levels
+  if (a.Mv <= 8) {
+    // 8 query heads on more than 2 KV heads need splits of one tile
+    if (G == 8 && HKV > 2 && a.tokens_per_split != 64) return hipErrorInvalidValue;
+    const int64_t pairs = S * a.nsplit;
     constexpr int64_t kCUs = 256;
-    int64_t wpw = (waves + kCUs - 1) / kCUs;
-    wpw = wpw < 1 ? 1 : (wpw > kWaves ? kWaves : wpw);
-    hipLaunchKernelGGL((attention4_kernel<G, HKV>), dim3(unsigned((waves + wpw - 1) / wpw)),
-                       dim3(unsigned(64 * wpw)), 0, stream, a, S);
+    int64_t ppw = (pairs + kCUs - 1) / kCUs;
+    ppw = ppw < 1 ? 1 : (ppw > kPairs ? kPairs : ppw);
+    hipLaunchKernelGGL((attention5_kernel<G, HKV>), dim3(unsigned((pairs + ppw - 1) / ppw)),
+                       dim3(unsigned(128 * ppw)), 0, stream, a, S);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((attention2_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);
