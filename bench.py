@@ -82,7 +82,10 @@ def run_config(torch, kvq, synth, w, bi, args, dev, extras=False, cpu_sample=Fal
     (record, samples for the CPU baseline or None)."""
     ck, cv = w.containers[bi]
     S, T, n, Hq, d = w.n_seqs, w.seq_len, w.n, w.n_q_heads, w.head_dim
-    plan = kvq.Plan(w.n_kv_heads, d, 8, 6, ck, cv, 128, 1.4)
+    layout = kvq.KVQ_LAYOUT_TILES if args.layout == "tiles" else kvq.KVQ_LAYOUT_ROWS
+    plan = kvq.Plan(w.n_kv_heads, d, 8, 6, ck, cv, 128, 1.4, layout=layout)
+    # bytes a container occupies in the cache (the tile layout rounds C up to 4)
+    sk, sv = plan.stored_bytes(0), plan.stored_bytes(1)
     nW = T // 128
     log(f"[bench] workload={w.name} S={S} T={T} Hq={Hq} Hkv={w.n_kv_heads} C=({ck},{cv})")
 
@@ -147,8 +150,8 @@ def run_config(torch, kvq, synth, w, bi, args, dev, extras=False, cpu_sample=Fal
     torch.cuda.empty_cache()
 
     # ---- read side: rotate copies when the working set would sit in cache
-    step_bytes = S * T * (ck + cv + 8) + S * nW * (n + 2)
-    kernel_bytes = S * T * (ck + cv + 8)
+    step_bytes = S * T * (sk + sv + 8) + S * nW * (n + 2)
+    kernel_bytes = S * T * (sk + sv + 8)
     copies = max(1, math.ceil((1 << 30) / step_bytes))
     if copies > 1:
         # one flat buffer per field, each copy at a 256-byte aligned stride
@@ -196,6 +199,7 @@ def run_config(torch, kvq, synth, w, bi, args, dev, extras=False, cpu_sample=Fal
         f"{kernel_ms:.4f} ms ({kgbs:.1f} GB/s, {kgbs / HBM_PEAK_GBS:.4f} of HBM peak) over {klaunch} launches")
     rec = {
         "workload": w.name, "budget_bits_per_elem": w.budgets[bi], "containers": [ck, cv], "levels": [8, 6],
+        "container_layout": args.layout,
         "shape": {"n_seqs": S, "batch": w.batch, "layers": w.layers, "seq_len": T, "q_heads": Hq,
                   "kv_heads": w.n_kv_heads, "head_dim": d},
         "bits_per_elem": round(plan.bits_per_elem(True), 4),
@@ -235,7 +239,7 @@ def run_config(torch, kvq, synth, w, bi, args, dev, extras=False, cpu_sample=Fal
         t1.record()
         torch.cuda.synchronize()
         ex_ms = t0.elapsed_time(t1) / args.steps
-        ex_bytes = S * n_pre * (ck + cv + 8) + S * (n_pre // W) * (n + 2) + S * r_len * n * 2 * 2
+        ex_bytes = S * n_pre * (sk + sv + 8) + S * (n_pre // W) * (n + 2) + S * r_len * n * 2 * 2
         reps = 3
         kvq.kvq_encode_append(plan, win_k, win_v, cache, T - W)
         torch.cuda.synchronize()
@@ -364,6 +368,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
                     help="time only the chosen workload (no per-config block of the other workloads)")
+    ap.add_argument("--layout", choices=("rows", "tiles"), default="tiles",
+                    help="container layout of the cache arrays (tiles: dword-interleaved 64-token tiles)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -404,7 +410,8 @@ def main():
                 rec, _ = run_config(torch, kvq, synth, wl, b, args, dev)
                 configs.append(rec)
     ck, cv = w.containers[bi]
-    traffic = measured_traffic(f"{w.name}@{ck}/{cv}", head["kernel_bytes"])
+    traffic = measured_traffic(f"{w.name}@{ck}/{cv}" + ("@tiles" if args.layout == "tiles" else ""),
+                               head["kernel_bytes"])
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, bi, samples)
     if cpu:
         log(f"[bench] cpu oracle: read side {cpu['value'] * 1e3:.3f} MB/s, encode "

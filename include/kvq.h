@@ -46,6 +46,24 @@ typedef enum {
 
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 
+/* How a cache array stores the containers of one side (container_layout).
+ * Either way a stream's container is the same C bytes ([D-Quant] §4.2 Eq. 3):
+ * the 4-byte little-endian final state, the payload the decoder reads
+ * forwards, zero padding.
+ *   KVQ_LAYOUT_ROWS   [n_seqs, capacity, C]: token t of sequence s at byte
+ *                     (s capacity + t) C, each container one row.
+ *   KVQ_LAYOUT_TILES  [n_seqs, capacity64, Cp]: capacity64 = capacity rounded
+ *                     up to a multiple of 64, Cp = C rounded up to a multiple
+ *                     of 4 (the extra bytes are zero).  Flat token
+ *                     g = s capacity64 + t: byte j of its container lies at
+ *                     (g / 64) 64 Cp + (j / 4) 256 + (g mod 64) 4 + j mod 4,
+ *                     i.e. dword k of the 64 containers of a tile side by
+ *                     side, so that a wave reading dword k of 64 consecutive
+ *                     tokens reads 256 contiguous bytes.  Decode attention
+ *                     with 9-level V alphabets and the fixed-width
+ *                     comparator take the row layout only. */
+typedef enum { KVQ_LAYOUT_ROWS = 0, KVQ_LAYOUT_TILES = 1 } kvq_layout;
+
 /* Configuration of one cache format ([D-Quant] §4.2, §4.4, §5.1: container
  * bytes, number of levels and the K/V split are free parameters; the page's
  * default is 331/231 bytes, 8/6 levels, alpha = 1.4, 2.26 bits per value). */
@@ -58,6 +76,7 @@ typedef struct {
   int32_t container_bytes_v;  /* C_V > 4                                      */
   int32_t mean_window;        /* W: power of two; tokens per key-mean window  */
   double sharpen_alpha;       /* alpha >= 1; probabilities p^alpha ([D-Quant] §4.4) */
+  int32_t container_layout;   /* kvq_layout of the cache arrays (0: rows)     */
 } kvq_params;
 
 /* Immutable plan: the integer rANS tables derived from the Gaussian
@@ -107,7 +126,9 @@ kvq_status kvq_plan_lambda_grid(const kvq_plan* plan, float* grid512);
 /* Storage cost in bits per value ([D-Quant] §3.1: symbols and metadata).
  * metadata != 0 counts, per token-layer, two fp16 (scale, offset) pairs and
  * the INT8 key mean of n values plus its fp16 scale per W tokens:
- * 8 (C_K + C_V + 8 + (n + 2) / W) / (2 n).  metadata == 0: containers only. */
+ * 8 (C_K + C_V + 8 + (n + 2) / W) / (2 n).  metadata == 0: containers only.
+ * With KVQ_LAYOUT_TILES the containers count at their stored size (C rounded
+ * up to a multiple of 4). */
 double kvq_bits_per_elem(const kvq_params* params, int metadata);
 
 /* Container sizes for a budget in bits per value (metadata included):
@@ -126,9 +147,11 @@ kvq_status kvq_workspace_bytes(const kvq_plan* plan, int op, int64_t n_seqs,
 
 /* Write side ([D-Quant] Figure 1, §4.2-§4.3, Appendix A Algorithm 1).
  *   k, v          [n_seqs, seq_len, Hkv, d] in `in_dtype` (fp32 or bf16)
- *   k_cont, v_cont out [n_seqs, seq_len, C_K] / [.., C_V] bytes; every row is
- *                 exactly C bytes: 4-byte little-endian final state, payload
- *                 (read forwards by the decoder), zero padding
+ *   k_cont, v_cont out [n_seqs, seq_len, C_K] / [.., C_V] bytes in the plan's
+ *                 container_layout (KVQ_LAYOUT_TILES: [n_seqs, seq_len rounded
+ *                 up to 64, C rounded up to 4]); every container is exactly C
+ *                 bytes: 4-byte little-endian final state, payload (read
+ *                 forwards by the decoder), zero padding
  *   k_so, v_so    out [n_seqs, seq_len, 2] fp16 bits: (scale, offset)
  *   k_mean_q      out [n_seqs, seq_len/W, n] int8 key channel means
  *   k_mean_scale  out [n_seqs, seq_len/W] fp16 bits
@@ -274,7 +297,10 @@ kvq_status kvq_decode_attention_fixed_width(const kvq_plan* plan, const void* q,
 
 /* Decodes containers back to symbol indices (Appendix A, Algorithm 2); a
  * verification helper.  side 0 = K table, 1 = V table.
- *   cont      [n_streams, C] bytes;  symbols out [n_streams, n] uint8
+ *   cont      [n_streams, C] bytes in the plan's container_layout (with
+ *             KVQ_LAYOUT_TILES, n_streams flat tokens of whole 64-token tiles,
+ *             i.e. n_seqs times the padded capacity);
+ *             symbols out [n_streams, n] uint8
  *   end_ok    nullable out [n_streams] uint32: 1 if the final state equals
  *             2^23 (a well-formed stream ends where the encoder started). */
 kvq_status kvq_decode_symbols(const kvq_plan* plan, int side, const uint8_t* cont,

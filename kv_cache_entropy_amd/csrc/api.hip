@@ -106,6 +106,15 @@ int fw_bits(int levels) {
 // Streams per encode workgroup: as many as fit (symbols staged at 4 bits,
 // plus the container image) in 56 KiB of LDS, up to one per lane of a wave,
 // since one lane per stream runs the rANS phase.
+// Bytes a container of C bytes occupies in the cache, and a sequence's cache
+// bytes, in the plan's layout (tiles: C rounded up to 4 bytes, the capacity
+// to 64 tokens).
+bool tiles(const kvq_params& P) { return P.container_layout == KVQ_LAYOUT_TILES; }
+int stored_bytes(const kvq_params& P, int C) { return tiles(P) ? (C + 3) / 4 * 4 : C; }
+int64_t seq_bytes(const kvq_params& P, int C, int64_t capacity) {
+  return tiles(P) ? (capacity + 63) / 64 * 64 * stored_bytes(P, C) : capacity * C;
+}
+
 int pick_spw(int64_t tokens, int n, int C) {
   for (int spw = 64; spw >= 4; spw >>= 1)
     if (tokens % spw == 0 && size_t(spw) * (size_t(n) / 2 + size_t(C)) <= 56u * 1024u) return spw;
@@ -206,7 +215,7 @@ kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_d
   if (n % 64 || n > 4096 || ((n / 64) & (n / 64 - 1)) || W < 4) return KVQ_EUNSUPPORTED;
   int fwb[2] = {0, 0};
   if (fixed_width) {
-    if (!plan->side[0].affine || !plan->side[1].affine) return KVQ_EUNSUPPORTED;
+    if (!plan->side[0].affine || !plan->side[1].affine || tiles(P)) return KVQ_EUNSUPPORTED;
     fwb[0] = fw_bits(P.levels_k);
     fwb[1] = fw_bits(P.levels_v);
     for (int side = 0; side < 2; ++side) {
@@ -216,8 +225,8 @@ kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_d
     }
   }
   const int64_t n_streams = n_seqs * n_tokens;
-  const int spw_k = pick_spw(n_tokens, n, P.container_bytes_k);
-  const int spw_v = pick_spw(n_tokens, n, P.container_bytes_v);
+  const int spw_k = pick_spw(n_tokens, n, stored_bytes(P, P.container_bytes_k));
+  const int spw_v = pick_spw(n_tokens, n, stored_bytes(P, P.container_bytes_v));
   if (!spw_k || !spw_v) return KVQ_EUNSUPPORTED;
   if (n_streams / 4 > int64_t(0x7FFFFFFF)) return KVQ_EUNSUPPORTED;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -256,6 +265,10 @@ kvq_status encode_impl(const kvq_plan* plan, const void* k, const void* v, kvq_d
     ea.hscale = plan->hadamard_scale;
     ea.spw = side == 0 ? spw_k : spw_v;
     ea.fw_bits = fwb[side];
+    const int C = side == 0 ? P.container_bytes_k : P.container_bytes_v;
+    ea.tiles = tiles(P) ? 1 : 0;
+    ea.cs = stored_bytes(P, C);
+    ea.seq_bytes = seq_bytes(P, C, capacity);
     ea.tabs = enc_tabs(plan, side);
     if (kvq::launch_encode(ea, n_streams, stream) != hipSuccess) return KVQ_EDEVICE;
   }
@@ -302,9 +315,12 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
   } else if (n_tokens % 64 || !kvq::attention2_supported(n_q_heads, G, d, P.levels_k, P.levels_v, W, affine)) {
     return KVQ_EUNSUPPORTED;
   }
+  // the tile layout is read by the split-wave kernel (V alphabets of up to 8 levels)
+  if (tiles(P) && (fixed_width || P.levels_v > 8)) return KVQ_EUNSUPPORTED;
   if (n_seqs > 65535) return KVQ_EUNSUPPORTED;
   // the attention kernel addresses one sequence's containers with 32-bit offsets
-  if (int64_t(n_tokens) * std::max(P.container_bytes_k, P.container_bytes_v) + 16 > INT32_MAX)
+  if (int64_t(n_tokens + 63) * std::max(stored_bytes(P, P.container_bytes_k), stored_bytes(P, P.container_bytes_v)) +
+          16 > INT32_MAX)
     return KVQ_EUNSUPPORTED;
   const WsLayout wl = ws_layout(plan, n_seqs, n_tokens, n_q_heads);
   if (workspace_bytes < wl.total) return KVQ_EWORKSPACE;
@@ -358,6 +374,11 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
     while ((1 << aa.log2W) < W) ++aa.log2W;
     aa.CK = P.container_bytes_k;
     aa.CV = P.container_bytes_v;
+    aa.tiles = tiles(P) ? 1 : 0;
+    aa.CKs = stored_bytes(P, P.container_bytes_k);
+    aa.CVs = stored_bytes(P, P.container_bytes_v);
+    aa.seq_bytes_k = seq_bytes(P, P.container_bytes_k, capacity);
+    aa.seq_bytes_v = seq_bytes(P, P.container_bytes_v, capacity);
     aa.tau = tau;
     aa.Mk = P.levels_k;
     aa.Mv = P.levels_v;
@@ -539,10 +560,13 @@ kvq_status kvq_decode_symbols(const kvq_plan* plan, int side, const uint8_t* con
                               void* hip_stream) {
   if (!plan || (side != 0 && side != 1) || !cont || !symbols || n_streams < 1) return KVQ_EINVAL;
   if (!aligned16(cont) || !aligned16(symbols) || (end_ok && !aligned16(end_ok))) return KVQ_EINVAL;
+  if (tiles(plan->params) && n_streams % 64) return KVQ_EINVAL;     // whole 64-token tiles
   kvq::DecSymArgs a;
   a.cont = cont;
   a.n_streams = n_streams;
   a.C = plan->side[side].container_bytes;
+  a.tiles = tiles(plan->params) ? 1 : 0;
+  a.cs = stored_bytes(plan->params, a.C);
   a.n = plan->n;
   a.sym = symbols;
   a.end_ok = end_ok;

@@ -551,6 +551,18 @@ __device__ inline uint4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// The 16-byte chunk at frame position F of a lane's container in the tile
+// layout: its four dwords lie 256 bytes apart (dword k of the tile's 64
+// containers side by side), so the wave's four loads each read 256
+// contiguous bytes.  off = the lane's dword offset + 64 F; kNoLoad stays out
+// of range for all four.
+__device__ inline uint4 load_chunk_tiles(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0),
+                    __builtin_amdgcn_raw_buffer_load_b32(rs, off + 256u, 0, 0),
+                    __builtin_amdgcn_raw_buffer_load_b32(rs, off + 512u, 0, 0),
+                    __builtin_amdgcn_raw_buffer_load_b32(rs, off + 768u, 0, 0));
+}
+
 struct Ring5 {
   uint32_t fo;          // buffer offset of the lane's 16-byte aligned frame
   uint32_t off;         // LDS offset of the lane's dword in row 0 of its ring
@@ -592,15 +604,18 @@ __device__ inline uint32_t ring5_window(const Ring5& r, const uint8_t* lds) {
 // Starts a container (cont_off: its byte offset in the sequence's buffer
 // resource): fills the ring with the first 64 frame bytes (chunks past the
 // container are not fetched) and reads the 4-byte little-endian initial state.
-template <int RS>
+// TL: the tile layout, cont_off the lane's dword-0 offset (frames start at 0).
+template <int RS, bool TL = false>
 __device__ inline uint32_t ring5_start(Ring5& r, uint8_t* lds, __amdgpu_buffer_rsrc_t rs, uint32_t cont_off,
                                        uint32_t C) {
-  const uint32_t off0 = cont_off & 15u;
+  const uint32_t off0 = TL ? 0u : cont_off & 15u;
   r.fo = cont_off - off0;
   r.lim = off0 + C;
   uint4 d[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) d[q] = load_chunk(rs, uint32_t(16 * q) < r.lim ? r.fo + 16u * q : kNoLoad);
+  for (int q = 0; q < 4; ++q)
+    d[q] = TL ? load_chunk_tiles(rs, uint32_t(16 * q) < r.lim ? r.fo + 1024u * q : kNoLoad)
+              : load_chunk(rs, uint32_t(16 * q) < r.lim ? r.fo + 16u * q : kNoLoad);
 #pragma unroll
   for (int q = 0; q < 4; ++q) ring5_write<RS>(lds, r.off, 16u * q, d[q]);
   r.F = 64u;
@@ -616,11 +631,11 @@ __device__ inline uint32_t ring5_start(Ring5& r, uint8_t* lds, __amdgpu_buffer_r
 // front.  Invariants (at most one byte per symbol): the bytes of the coming 16
 // symbols are written before they are read, and a chunk never overwrites
 // bytes not yet consumed.
-template <int S, int RS>
+template <int S, int RS, bool TL = false>
 __device__ inline void ring5_block(Ring5& r, uint8_t* lds, __amdgpu_buffer_rsrc_t rs) {
   if (r.ppos[S] != kNoChunk) ring5_write<RS>(lds, r.off, r.ppos[S], r.pend[S]);
   const bool real = (r.F < r.lim) && (r.F - r.P <= 48u);
-  r.pend[S] = load_chunk(rs, real ? r.fo + r.F : kNoLoad);
+  r.pend[S] = TL ? load_chunk_tiles(rs, real ? r.fo + 64u * r.F : kNoLoad) : load_chunk(rs, real ? r.fo + r.F : kNoLoad);
   r.ppos[S] = real ? r.F : kNoChunk;
   r.F += real ? 16u : 0u;
 }
@@ -830,7 +845,8 @@ __device__ inline void pv_half_int(const uint8_t* vch, int lane, int qn, const u
   }
 }
 
-template <int G, int HKV>
+// TL: containers in the tile layout (KVQ_LAYOUT_TILES), rows otherwise.
+template <int G, int HKV, bool TL>
 __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a, int64_t S) {
   using Lay = Lay5<G, HKV>;
   constexpr int HQ = Lay::HQ;
@@ -940,8 +956,8 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
 #pragma unroll
       for (int t = 0; t < 2; ++t) qnx[m][t] = kQPrefetch ? qop[(m * 32 + qc0 + 8 * t) * 4 + qn] : uint4{};
 
-    const uint8_t* const kseq = a.k_cont + s * a.T_cap * a.CK;
-    const __amdgpu_buffer_rsrc_t rsK = seq_rsrc(kseq, uint32_t(a.T * a.CK));
+    const uint8_t* const kseq = a.k_cont + s * (TL ? a.seq_bytes_k : a.T_cap * a.CK);
+    const __amdgpu_buffer_rsrc_t rsK = seq_rsrc(kseq, uint32_t(a.T * (TL ? a.CKs : a.CK)));
     const uint32_t misK = uint32_t(reinterpret_cast<uintptr_t>(kseq) & 15u);
     uint32_t xk = 0;
     float sk = 0.f, ok = 0.f, svK = 0.f, ovK = 0.f;
@@ -951,7 +967,11 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
       for (int g = 0; g < HKV; ++g) {
         if (g == 0) {
           const int64_t row = s * a.T_cap + tK + lane;
-          xk = ring5_start<RS>(rk, lds, rsK, misK + uint32_t(tK + lane) * uint32_t(a.CK), uint32_t(a.CK));
+          xk = ring5_start<RS, TL>(
+              rk, lds, rsK,
+              TL ? misK + uint32_t(tK) * uint32_t(a.CKs) + uint32_t(lane) * 4u
+                 : misK + uint32_t(tK + lane) * uint32_t(a.CK),
+              uint32_t(a.CK));
           sk = h2f(a.k_so[2 * row]);
           ok = h2f(a.k_so[2 * row + 1]);
           svK = h2f(a.v_so[2 * row]);
@@ -991,8 +1011,8 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
           for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
             for (int bh = 0; bh < 2; ++bh) {
-              if (bh == 1) ring5_block<1, RS>(rk, lds, rsK);
-              else ring5_block<0, RS>(rk, lds, rsK);
+              if (bh == 1) ring5_block<1, RS, TL>(rk, lds, rsK);
+              else ring5_block<0, RS, TL>(rk, lds, rsK);
 #pragma unroll
               for (int cc = 0; cc < 4; ++cc) {
                 uint32_t e[4];
@@ -1108,8 +1128,8 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int m = 0; m < NGM; ++m) O[g][c][m] = float4_t{0.f, 0.f, 0.f, 0.f};
-  const uint8_t* const vseq = a.v_cont + s * a.T_cap * a.CV;
-  const __amdgpu_buffer_rsrc_t rsV = seq_rsrc(vseq, uint32_t(a.T * a.CV));
+  const uint8_t* const vseq = a.v_cont + s * (TL ? a.seq_bytes_v : a.T_cap * a.CV);
+  const __amdgpu_buffer_rsrc_t rsV = seq_rsrc(vseq, uint32_t(a.T * (TL ? a.CVs : a.CV)));
   const uint32_t misV = uint32_t(reinterpret_cast<uintptr_t>(vseq) & 15u);
   uint32_t xv = 0;
   if constexpr (PERHEAD) {
@@ -1117,7 +1137,10 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
       const int64_t tV = tb + 64 * i;
 #pragma unroll 1
       for (int g = 0; g < HKV; ++g) {
-        if (g == 0) xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
+        if (g == 0) xv = ring5_start<RS, TL>(rv, lds, rsV,
+                                             TL ? misV + uint32_t(tV) * uint32_t(a.CVs) + uint32_t(lane) * 4u
+                                                : misV + uint32_t(tV + lane) * uint32_t(a.CV),
+                                             uint32_t(a.CV));
         const uint16_t* const wv = wts;
         const uint16_t* const wv_lo = wv + NW * 64;
         float4_t Oc[2][NGM];
@@ -1132,8 +1155,8 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
 #pragma unroll
             for (int bh = 0; bh < 2; ++bh) {
               const int b4 = 2 * b2 + bh;
-              if (bh == 1) ring5_block<1, RS>(rv, lds, rsV);
-              else ring5_block<0, RS>(rv, lds, rsV);
+              if (bh == 1) ring5_block<1, RS, TL>(rv, lds, rsV);
+              else ring5_block<0, RS, TL>(rv, lds, rsV);
 #pragma unroll
               for (int cc = 0; cc < 4; ++cc) {
                 const uint32_t winV = ring5_window<RS>(rv, lds);
@@ -1175,7 +1198,10 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
     const int64_t tV = tb + 64 * i;
 #pragma unroll 1
     for (int g = 0; g < HKV; ++g) {
-      if (g == 0) xv = ring5_start<RS>(rv, lds, rsV, misV + uint32_t(tV + lane) * uint32_t(a.CV), uint32_t(a.CV));
+      if (g == 0) xv = ring5_start<RS, TL>(rv, lds, rsV,
+                                             TL ? misV + uint32_t(tV) * uint32_t(a.CVs) + uint32_t(lane) * 4u
+                                                : misV + uint32_t(tV + lane) * uint32_t(a.CV),
+                                             uint32_t(a.CV));
       const uint16_t* const wv = wts;
       const uint16_t* const wv_lo = wv + NW * 64;
       auto rescale = [&]() {
@@ -1204,8 +1230,8 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
 #pragma unroll
           for (int bh = 0; bh < 2; ++bh) {
             const int b4 = 2 * b2 + bh;
-            if (bh == 1) ring5_block<1, RS>(rv, lds, rsV);
-            else ring5_block<0, RS>(rv, lds, rsV);
+            if (bh == 1) ring5_block<1, RS, TL>(rv, lds, rsV);
+            else ring5_block<0, RS, TL>(rv, lds, rsV);
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
               const uint32_t winV = ring5_window<RS>(rv, lds);
@@ -1551,8 +1577,11 @@ static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stre
     constexpr int64_t kCUs = 256;
     int64_t ppw = (pairs + kCUs - 1) / kCUs;
     ppw = ppw < 1 ? 1 : (ppw > kPairs ? kPairs : ppw);
-    hipLaunchKernelGGL((attention5_kernel<G, HKV>), dim3(unsigned((pairs + ppw - 1) / ppw)),
-                       dim3(unsigned(128 * ppw)), 0, stream, a, S);
+    const dim3 grid(unsigned((pairs + ppw - 1) / ppw)), block(unsigned(128 * ppw));
+    if (a.tiles)
+      hipLaunchKernelGGL((attention5_kernel<G, HKV, true>), grid, block, 0, stream, a, S);
+    else
+      hipLaunchKernelGGL((attention5_kernel<G, HKV, false>), grid, block, 0, stream, a, S);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((attention2_kernel<G, HKV>), dim3(a.nsplit, unsigned(S)), dim3(64), 0, stream, a);

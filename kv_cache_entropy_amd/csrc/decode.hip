@@ -32,8 +32,11 @@ __global__ __launch_bounds__(256) void decode_symbols_kernel(DecSymArgs a) {
   __syncthreads();
   const int64_t s = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (s >= a.n_streams) return;
-  const uint8_t* p = a.cont + s * a.C;
-  uint32_t x = uint32_t(p[0]) | (uint32_t(p[1]) << 8) | (uint32_t(p[2]) << 16) | (uint32_t(p[3]) << 24);
+  // byte j of the stream: row layout s C + j; tile layout, dword j / 4 of the
+  // 64 containers of a tile side by side
+  const uint8_t* const p = a.tiles ? a.cont + (s >> 6) * 64 * int64_t(a.cs) + (s & 63) * 4 : a.cont + s * a.C;
+  auto at = [&](int j) -> uint32_t { return a.tiles ? p[(j >> 2) * 256 + (j & 3)] : p[j]; };
+  uint32_t x = at(0) | (at(1) << 8) | (at(2) << 16) | (at(3) << 24);
   int ptr = 4;
   uint8_t* out = a.sym + s * a.n;
   for (int i = 0; i < a.n; ++i) {
@@ -43,7 +46,7 @@ __global__ __launch_bounds__(256) void decode_symbols_kernel(DecSymArgs a) {
     // a well-formed stream needs at most one byte per symbol; the bound keeps
     // malformed input from looping
     for (int r = 0; r < 2 && x < kStateLow; ++r) {
-      const uint32_t b = ptr < a.C ? p[ptr] : 0u;
+      const uint32_t b = ptr < a.C ? at(ptr) : 0u;
       x = (x << 8) | b;
       ++ptr;
     }

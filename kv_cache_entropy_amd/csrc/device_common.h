@@ -52,6 +52,9 @@ struct EncodeArgs {
   float hscale;
   int spw;                     // streams per workgroup (multiple of 4)
   int fw_bits;                 // 0: rANS + drift; 1/2/4/8: fixed-width comparator
+  int tiles;                   // KVQ_LAYOUT_TILES: dword k of a 64-token tile's containers side by side
+  int cs;                      // bytes a container occupies in the cache (C, or C rounded up to 4)
+  int64_t seq_bytes;           // cache bytes per sequence (tiles: capacity rounded up to 64, times cs)
   EncTabs tabs;
 };
 
@@ -72,6 +75,8 @@ struct DecSymArgs {
   int C, n;
   uint8_t* sym;
   uint32_t* end_ok;
+  int tiles;                   // KVQ_LAYOUT_TILES (n_streams is then a multiple of 64)
+  int cs;                      // bytes a container occupies (C, or C rounded up to 4)
   uint32_t dec[256];
 };
 
@@ -112,6 +117,9 @@ struct Attn2Args {
   uint32_t lvk[kMaxLevels];   // fp16 bits of the key levels
   uint32_t lbv[kMaxLevels];   // low bytes of the fp16 value levels (0 when affine)
   int v_lo_nonzero;           // some value level has a nonzero low byte
+  int tiles;                   // KVQ_LAYOUT_TILES containers (split-wave kernel only)
+  int CKs, CVs;                // bytes a container occupies (C, or C rounded up to 4)
+  int64_t seq_bytes_k, seq_bytes_v;   // cache bytes per sequence
   // decode-table entries of the fused kernels, slot z = state mod 256: f | (z - c) << 8
   // in the low half; the high half holds the fp16 bits of the key level (K) or
   // the level index (V)

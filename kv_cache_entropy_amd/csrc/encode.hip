@@ -456,8 +456,9 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int SPW = a.spw;
   const int n = a.n, C = a.tabs.container_bytes, M = a.tabs.levels;
+  const int CS = a.cs;                         // a container's bytes in the image and the cache
   uint8_t* sym = dyn;                          // [SPW][n / 2]: two 4-bit symbols per byte
-  uint8_t* img = dyn + size_t(SPW) * (n / 2);  // [SPW][C]
+  uint8_t* img = dyn + size_t(SPW) * (n / 2);  // [SPW][CS]
   for (int i = tid; i < 512; i += 256) sh.lambda[i] = a.tabs.lambda[i];
   if (tid < kMaxLevels) {
     sh.level[tid] = a.tabs.level[tid];
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
       nearest<NPL>(x, s, o, M, sh.level, m);
       refit<NPL>(x, m, s, o, n, sh.level, s16, o16);
       nearest<NPL>(x, __half2float(s16), __half2float(o16), M, sh.level, m);
-      if constexpr (FW) fw_pack_lane<NPL, FWB>(m, reinterpret_cast<uint32_t*>(img + size_t(sl) * C), lane);
+      if constexpr (FW) fw_pack_lane<NPL, FWB>(m, reinterpret_cast<uint32_t*>(img + size_t(sl) * CS), lane);
     } else {
       uint8_t near[NPL];
       if (NPL * kDriftCache <= 128 && M <= kDriftCache) {
@@ -536,17 +537,33 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   const int64_t ost0 = seq0 * a.T_cap + a.t_off + (stream0 - seq0 * a.T);
   uint32_t overrun = 0;
   if (tid < SPW) {
-    if constexpr (!FW)
-      overrun = rans_encode_lane(sym + size_t(tid) * (n / 2), n, img + size_t(tid) * C, C, sh) ? 0u : 1u;
+    if constexpr (!FW) {
+      overrun = rans_encode_lane(sym + size_t(tid) * (n / 2), n, img + size_t(tid) * CS, C, sh) ? 0u : 1u;
+      for (int j = C; j < CS; ++j) img[size_t(tid) * CS + j] = 0;
+    }
     reinterpret_cast<uint32_t*>(a.so)[ost0 + tid] = so_sh[tid];
   }
   __syncthreads();
-  // SPW * C is a multiple of 4 (SPW is a multiple of 4); ost0 * C is a multiple of 4
-  // because ost0 is a multiple of SPW
-  const int nwords = SPW * C / 4;
-  uint32_t* gdst = reinterpret_cast<uint32_t*>(a.cont + ost0 * C);
   const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(img);
-  for (int i = tid; i < nwords; i += 256) gdst[i] = ssrc[i];
+  if (a.tiles) {
+    // dword k of cache token t at (t / 64) 64 CS + k 256 + (t mod 64) 4 in its
+    // sequence; consecutive threads take consecutive tokens of one dword k
+    const int dps = CS / 4;
+    const int64_t t0 = a.t_off + (stream0 - seq0 * a.T);
+    uint8_t* const seqb = a.cont + seq0 * a.seq_bytes;
+    for (int i = tid; i < SPW * dps; i += 256) {
+      const int j = i % SPW, kd = i / SPW;
+      const int64_t t = t0 + j;
+      *reinterpret_cast<uint32_t*>(seqb + (t >> 6) * (64 * int64_t(CS)) + int64_t(kd) * 256 + (t & 63) * 4) =
+          ssrc[j * dps + kd];
+    }
+  } else {
+    // SPW * C is a multiple of 4 (SPW is a multiple of 4); ost0 * C is a
+    // multiple of 4 because ost0 is a multiple of SPW
+    const int nwords = SPW * C / 4;
+    uint32_t* gdst = reinterpret_cast<uint32_t*>(a.cont + ost0 * C);
+    for (int i = tid; i < nwords; i += 256) gdst[i] = ssrc[i];
+  }
   if (a.stats) {
     if (lane == 0) {
       if (fb1) atomicAdd(a.stats + 0, (unsigned long long)fb1);
@@ -566,7 +583,7 @@ hipError_t launch_key_mean(const KeyMeanArgs& a, int64_t n_windows, hipStream_t 
 }
 
 hipError_t launch_encode(const EncodeArgs& a, int64_t n_streams, hipStream_t stream) {
-  const size_t lds = size_t(a.spw) * (size_t(a.n) / 2 + size_t(a.tabs.container_bytes));
+  const size_t lds = size_t(a.spw) * (size_t(a.n) / 2 + size_t(a.cs));
   const dim3 grid(unsigned(n_streams / a.spw)), block(256);
   if (a.fw_bits) {
     const int key = (a.n / 64) * 16 + a.fw_bits;

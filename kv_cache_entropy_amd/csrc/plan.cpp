@@ -277,6 +277,7 @@ kvq_status kvq_plan_create_levels(const kvq_params* params, const float* values_
       p.container_bytes_k > 65536 || p.container_bytes_v > 65536)
     return KVQ_EINVAL;
   if (!pow2(p.mean_window)) return KVQ_EINVAL;
+  if (p.container_layout != KVQ_LAYOUT_ROWS && p.container_layout != KVQ_LAYOUT_TILES) return KVQ_EINVAL;
   if (!(p.sharpen_alpha >= 1.0) || !(p.sharpen_alpha <= 16.0)) return KVQ_EINVAL;
   kvq_plan* plan = new (std::nothrow) kvq_plan;
   if (!plan) return KVQ_ENOMEM;
@@ -344,7 +345,9 @@ kvq_status kvq_model_probs(int32_t levels, int32_t n, double alpha, double* prob
 double kvq_bits_per_elem(const kvq_params* p, int metadata) {
   if (!p) return -1.0;
   const double n = double(p->n_kv_heads) * p->head_dim;
-  double bytes = double(p->container_bytes_k) + p->container_bytes_v;
+  const bool tiles = p->container_layout == KVQ_LAYOUT_TILES;
+  const auto stored = [tiles](int32_t c) { return double(tiles ? (c + 3) / 4 * 4 : c); };
+  double bytes = stored(p->container_bytes_k) + stored(p->container_bytes_v);
   if (metadata) bytes += 2 * (2 + 2) + (n + 2) / double(p->mean_window);
   return 8.0 * bytes / (2.0 * n);
 }

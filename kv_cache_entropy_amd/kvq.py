@@ -30,7 +30,11 @@ class kvq_params(ctypes.Structure):
     _fields_ = [("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("levels_k", ctypes.c_int32), ("levels_v", ctypes.c_int32),
                 ("container_bytes_k", ctypes.c_int32), ("container_bytes_v", ctypes.c_int32),
-                ("mean_window", ctypes.c_int32), ("sharpen_alpha", ctypes.c_double)]
+                ("mean_window", ctypes.c_int32), ("sharpen_alpha", ctypes.c_double),
+                ("container_layout", ctypes.c_int32)]
+
+
+KVQ_LAYOUT_ROWS, KVQ_LAYOUT_TILES = 0, 1
 
 
 _lib = None
@@ -114,8 +118,9 @@ def _cache_ptrs(plan, S, rows, k_cont, v_cont, k_so, v_so, k_mean_q, k_mean_scal
     """Pointers of the six cache arrays for S sequences of `rows` token rows."""
     p = plan.params
     nW = rows // p.mean_window
-    return (_ptr(k_cont, S * rows * p.container_bytes_k, "k_cont"),
-            _ptr(v_cont, S * rows * p.container_bytes_v, "v_cont"),
+    cr = plan.cache_rows(rows)
+    return (_ptr(k_cont, S * cr * plan.stored_bytes(0), "k_cont"),
+            _ptr(v_cont, S * cr * plan.stored_bytes(1), "v_cont"),
             _ptr(k_so, S * rows * 4, "k_so"), _ptr(v_so, S * rows * 4, "v_so"),
             _ptr(k_mean_q, S * nW * plan.n, "k_mean_q"), _ptr(k_mean_scale, S * nW * 2, "k_mean_scale"))
 
@@ -146,9 +151,10 @@ class Plan:
     """Owns a kvq_plan (host-side tables of one cache format)."""
 
     def __init__(self, n_kv_heads, head_dim, levels_k=8, levels_v=6, container_bytes_k=331,
-                 container_bytes_v=231, mean_window=128, sharpen_alpha=1.4, values_k=None, values_v=None):
+                 container_bytes_v=231, mean_window=128, sharpen_alpha=1.4, values_k=None, values_v=None,
+                 layout=KVQ_LAYOUT_ROWS):
         self.params = kvq_params(n_kv_heads, head_dim, levels_k, levels_v, container_bytes_k,
-                                 container_bytes_v, mean_window, sharpen_alpha)
+                                 container_bytes_v, mean_window, sharpen_alpha, layout)
         h = ctypes.c_void_p()
         if values_k is None and values_v is None:
             _check("kvq_plan_create", lib().kvq_plan_create(ctypes.byref(self.params), ctypes.byref(h)))
@@ -157,6 +163,20 @@ class Plan:
             _check("kvq_plan_create_levels", lib().kvq_plan_create_levels(
                 ctypes.byref(self.params), arr(values_k), arr(values_v), ctypes.byref(h)))
         self.handle = h
+
+    @property
+    def tiles(self):
+        return self.params.container_layout == KVQ_LAYOUT_TILES
+
+    def stored_bytes(self, side):
+        """Bytes a container of side 0 (K) / 1 (V) occupies in the cache."""
+        C = self.params.container_bytes_k if side == 0 else self.params.container_bytes_v
+        return (C + 3) // 4 * 4 if self.tiles else C
+
+    def cache_rows(self, tokens):
+        """Token rows a cache of `tokens` tokens per sequence holds (whole 64-token
+        tiles in the tile layout)."""
+        return (tokens + 63) // 64 * 64 if self.tiles else tokens
 
     def levels(self, side):
         """Level values v_m as stored (floats) for side 0 (K) / 1 (V)."""
@@ -257,9 +277,9 @@ def kvq_decode_attention_noalloc(plan, q, k_cont, v_cont, k_so, v_so, k_mean_q, 
 
 def kvq_encode_append(plan, k, v, cache, token_offset, stats=None, stream=None):
     """Encodes k, v [S, T', Hkv, d] into rows [token_offset, token_offset + T') of `cache`
-    (the dict of alloc_cache, whose second dimension is the capacity)."""
+    (the dict of alloc_cache; the capacity is the second dimension of its k_so)."""
     dt, S, T, kp, vp = _kv_ptrs(plan, k, v)
-    cap = int(cache["k_cont"].shape[1])
+    cap = int(cache["k_so"].shape[1])           # the capacity (container arrays may round it up)
     cp = _cache_ptrs(plan, S, cap, cache["k_cont"], cache["v_cont"], cache["k_so"], cache["v_so"],
                      cache["k_mean_q"], cache["k_mean_scale"])
     _check("kvq_encode_append", lib().kvq_encode_append(
@@ -269,14 +289,14 @@ def kvq_encode_append(plan, k, v, cache, token_offset, stats=None, stream=None):
 
 def kvq_decode_attention_ex(plan, q, cache, n_tokens, res_k, res_v, res_len, out, workspace,
                             out_f32=None, softmax_scale=0.0, stream=None):
-    """Attention over rows [0, n_tokens) of `cache` (capacity = its second dimension;
+    """Attention over rows [0, n_tokens) of `cache` (capacity = k_so's second dimension;
     may be None when n_tokens == 0) and rows [0, res_len) of res_k / res_v
     [S, R_cap, Hkv, d] bf16 (may be None when res_len == 0)."""
     if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
         raise TypeError("q and out must be bfloat16")
     S, Hq = int(q.shape[0]), int(q.shape[1])
     c = cache or {}
-    cap = int(c["k_cont"].shape[1]) if cache is not None else 0
+    cap = int(c["k_so"].shape[1]) if cache is not None else 0
     rcap = int(res_k.shape[1]) if res_k is not None else 0
     if res_k is not None and (res_k.dtype != torch.bfloat16 or res_v.dtype != torch.bfloat16):
         raise TypeError("res_k and res_v must be bfloat16")
@@ -322,9 +342,9 @@ def kvq_decode_attention_fixed_width(plan, q, k_cont, v_cont, k_so, v_so, k_mean
 
 def kvq_decode_symbols(plan, side, cont, symbols, end_ok=None, stream=None):
     """cont: [..., C] uint8; symbols: [..., n] uint8; end_ok: nullable int32/uint32-sized."""
-    C = plan.params.container_bytes_k if side == 0 else plan.params.container_bytes_v
+    C = plan.stored_bytes(side)
     if cont.shape[-1] != C:
-        raise ValueError(f"cont: last dimension must be the container size {C}")
+        raise ValueError(f"cont: last dimension must be the stored container size {C}")
     n_streams = cont.numel() // C
     _check("kvq_decode_symbols", lib().kvq_decode_symbols(
         plan.handle, side, _ptr(cont, name="cont"), n_streams, _ptr(symbols, n_streams * plan.n, "symbols"),
@@ -347,11 +367,24 @@ def alloc_cache(plan, n_seqs, seq_len, device="cuda"):
     p = plan.params
     nW = seq_len // p.mean_window
     e = lambda *shape, dtype: torch.empty(*shape, dtype=dtype, device=device)
+    rows = plan.cache_rows(seq_len)
     return {
-        "k_cont": e(n_seqs, seq_len, p.container_bytes_k, dtype=torch.uint8),
-        "v_cont": e(n_seqs, seq_len, p.container_bytes_v, dtype=torch.uint8),
+        "k_cont": e(n_seqs, rows, plan.stored_bytes(0), dtype=torch.uint8),
+        "v_cont": e(n_seqs, rows, plan.stored_bytes(1), dtype=torch.uint8),
         "k_so": e(n_seqs, seq_len, 2, dtype=torch.int16),
         "v_so": e(n_seqs, seq_len, 2, dtype=torch.int16),
         "k_mean_q": e(n_seqs, nW, plan.n, dtype=torch.int8),
         "k_mean_scale": e(n_seqs, nW, dtype=torch.int16),
     }
+
+
+def container_rows(plan, side, cont, n_tokens):
+    """The containers of a cache array as [S, n_tokens, C] rows (a copy; for
+    inspection and tests, not the read path): in the tile layout, dword k of
+    token g sits at dword (g / 64) 64 Cp / 4 + k 64 + g mod 64 of the array."""
+    C = plan.params.container_bytes_k if side == 0 else plan.params.container_bytes_v
+    if not plan.tiles:
+        return cont[:, :n_tokens, :C]
+    S, rows, Cp = int(cont.shape[0]), int(cont.shape[1]), int(cont.shape[2])
+    t = cont.reshape(S, rows // 64, Cp // 4, 64, 4).permute(0, 1, 3, 2, 4).reshape(S, rows, Cp)
+    return t[:, :n_tokens, :C].contiguous()
