@@ -864,8 +864,11 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pw = w >> 1;              // pair within the workgroup
-  const bool kwave = (w & 1) == 0;
+  // waves 0 .. np-1 decode K, waves np .. 2np-1 decode V (pair w mod np), so
+  // that every SIMD (wave index mod 4) hosts K and V waves alike
+  const int np = int(blockDim.x >> 7);
+  const bool kwave = w < np;
+  const int pw = kwave ? w : w - np;  // pair within the workgroup
 
   // Decode tables: entry idx of the replicated table is the host's entry for
   // slot idx / NREP (one load from the kernel arguments).
