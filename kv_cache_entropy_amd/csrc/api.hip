@@ -396,7 +396,10 @@ kvq_status attention_impl(const kvq_plan* plan, const void* q, int32_t n_q_heads
     for (int z = 0; z < 256; ++z) {
       const uint32_t dk = plan->side[0].dec[z];
       aa.tabk[z] = (dk & 0xFFFFu) | (plan->side[0].fp16_bits[(dk >> 16) & 0xFFu] << 16);
-      aa.tabv[z] = plan->side[1].dec[z];
+      // integer value levels (zero fp16 low bytes): the level's fp16 high byte in
+      // place of its index, so the product needs no lookup
+      const uint32_t dv = plan->side[1].dec[z];
+      aa.tabv[z] = aa.v_lo_nonzero ? dv : (dv & 0xFFFFu) | (plan->side[1].fp16_hi[(dv >> 16) & 0xFFu] << 16);
     }
     size_t slot = 0;
     const bool timed = timer_begin(stream, &slot);

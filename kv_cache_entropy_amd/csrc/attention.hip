@@ -505,8 +505,8 @@ __global__ __launch_bounds__(64, 2) void attention2_kernel(Attn2Args a) {
 
 // ------------------------------------------- LDS rings and decode tables
 // Decode-table entries are 32-bit: f | (z - c) << 8 | payload, the payload
-// being the fp16 bits of the level (K) or the level index (V) in bits
-// 16..31.  Replicated tables put replica r of a slot at a bank of its own, and
+// being the fp16 bits of the level (K) or, in bits 16..23, the level's fp16
+// high byte (V with integer levels) or its index (other V levels).  Replicated tables put replica r of a slot at a bank of its own, and
 // lane l reads replica l mod R.
 // A lane's ring holds container bytes [16 rows of 4]: frame byte p sits in
 // row (p / 4) mod 16, byte p mod 4 of the lane's own dword of that row, so the
@@ -726,7 +726,7 @@ __device__ inline void pv_half(const uint8_t* vch, int lane, int qn, const uint1
 // then posts s + 1; the V wave decodes the first half of step s (with at most
 // 4 pairs per workgroup, both halves) before it waits for that post.
 //
-// LDS map: per pair (VCH: [64 ch][68] int8 V levels of a half step; WTS: one
+// LDS map: per pair (VCH: [64 ch][68] V level bytes of a half step; WTS: one
 // step's [hi/lo][NW][64] fp16 weights; ALV: the step's rescale factors, a grow
 // flag and the two counters; RUN: running max, sums and the tile's affine
 // terms), then the pairs' rings (K ring 2p, V ring 2p + 1, 17 rows of 64
@@ -811,11 +811,12 @@ __device__ __forceinline__ void pair_post(uint32_t* counter, uint32_t value, int
   if (lane == 0) __hip_atomic_store(counter, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// pv_half for integer V levels (every fp16 level has a zero low byte): one
-// v_perm looks up the 4 high bytes, two more place them over zero low bytes.
+// pv_half for integer V levels (every fp16 level has a zero low byte): the
+// chunk holds the levels' fp16 high bytes (the V table entries carry them in
+// place of the level index), and two v_perms place them over zero low bytes.
 template <int NGM>
 __device__ inline void pv_half_int(const uint8_t* vch, int lane, int qn, const uint16_t* wv, const uint16_t* wv_lo,
-                                   uint32_t lutHi, uint32_t lutLo, float4_t (&O)[NGM]) {
+                                   float4_t (&O)[NGM]) {
   // 4 columns per batch: every LDS load of the batch first, then the
   // lookups and products
 #pragma unroll
@@ -833,7 +834,7 @@ __device__ inline void pv_half_int(const uint8_t* vch, int lane, int qn, const u
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t hb = __builtin_amdgcn_perm(lutHi, lutLo, idx[u]);
+      const uint32_t hb = idx[u];
       const half4_t B =
           as_half4(__builtin_amdgcn_perm(0u, hb, 0x010C000Cu), __builtin_amdgcn_perm(0u, hb, 0x030C020Cu));
 #pragma unroll
@@ -1109,13 +1110,12 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   const uint32_t toffV = opaque(PERM ? 64u + uint32_t(lane % 16) * 4u : Lay::TABV + uint32_t(lane % Lay::REPS) * 4u);
   Ring5 rv;
   rv.off = opaque(ring_off(2 * pw + 1));
-  // fp16 bytes of the V levels as v_perm lookups, kept in VGPRs (the empty asm
-  // stops the compiler from rebuilding them from SGPRs in the PV loop)
-  uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
-  uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
+  // fp16 bytes of the V levels as v_perm lookups (non-integer levels only:
+  // for integer levels the decoded entries already hold the high bytes)
+  const uint32_t lutLo = a.hbv[0] | (a.hbv[1] << 8) | (a.hbv[2] << 16) | (a.hbv[3] << 24);
+  const uint32_t lutHi = a.hbv[4] | (a.hbv[5] << 8) | (a.hbv[6] << 16) | (a.hbv[7] << 24);
   const uint32_t lutLo2 = a.lbv[0] | (a.lbv[1] << 8) | (a.lbv[2] << 16) | (a.lbv[3] << 24);
   const uint32_t lutHi2 = a.lbv[4] | (a.lbv[5] << 8) | (a.lbv[6] << 16) | (a.lbv[7] << 24);
-  asm volatile("" : "+v"(lutLo), "+v"(lutHi));
   const bool lo_levels = a.v_lo_nonzero != 0;
   // A workgroup of at most 4 pairs leaves pairs 4..7's areas unused: there
   // the V wave keeps the second half of a step in pair pw + 4's VCH area and
@@ -1177,7 +1177,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
           if (lo_levels)
             pv_half<NGM, true>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, Oc[ch]);
           else
-            pv_half_int<NGM>(vch, lane, qn, wv, wv_lo, lutHi, lutLo, Oc[ch]);
+            pv_half_int<NGM>(vch, lane, qn, wv, wv_lo, Oc[ch]);
           wave_lds_fence();
         }
         pair_post(done, ++step, lane);
@@ -1222,7 +1222,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
         if (lo_levels)
           pv_half<NGM, true>(vc, lane, qn, wv, wv_lo, lutHi, lutLo, lutHi2, lutLo2, O[0][ch]);
         else
-          pv_half_int<NGM>(vc, lane, qn, wv, wv_lo, lutHi, lutLo, O[0][ch]);
+          pv_half_int<NGM>(vc, lane, qn, wv, wv_lo, O[0][ch]);
         wave_lds_fence();
       };
 #pragma unroll
@@ -1571,8 +1571,9 @@ bool attention2_supported(int Hq, int G, int d, int levels_k, int levels_v, int 
 
 template <int G, int HKV>
 static hipError_t launch_attn2_t(const Attn2Args& a, int64_t S, hipStream_t stream) {
-  // the split-wave kernel keeps V levels as int8 and maps them to fp16 with an
-  // 8-entry lookup, so it serves V alphabets of up to 8 levels
+  // the split-wave kernel keeps V levels as bytes (fp16 high byte or, for
+  // non-integer levels, an index into an 8-entry lookup), so it serves V
+  // alphabets of up to 8 levels
   if (a.Mv <= 8) {
     // 8 query heads on more than 2 KV heads need splits of one tile
     if (G == 8 && HKV > 2 && a.tokens_per_split != 64) return hipErrorInvalidValue;

@@ -121,8 +121,9 @@ struct Attn2Args {
   int CKs, CVs;                // bytes a container occupies (C, or C rounded up to 4)
   int64_t seq_bytes_k, seq_bytes_v;   // cache bytes per sequence
   // decode-table entries of the fused kernels, slot z = state mod 256: f | (z - c) << 8
-  // in the low half; the high half holds the fp16 bits of the key level (K) or
-  // the level index (V)
+  // in the low half; the high half holds the fp16 bits of the key level (K) or,
+  // for V, the level's fp16 high byte when every value level is an integer
+  // (v_lo_nonzero == 0), else the level index
   uint32_t tabk[256], tabv[256];
 };
 
