@@ -67,14 +67,14 @@ def measured_traffic(workload_key, bytes_hint):
     return rec.get("hbm_bytes_per_launch")
 
 
-def kernel_name(w, levels_v=6):
-    """The fused kernel the library launches for this head layout (its dispatch
-    rule: K and V decoded in separate waves for V alphabets of up to 8 levels;
-    a single-wave kernel otherwise)."""
+def kernel_name(w, levels_v=6, tiles=True):
+    """The fused kernel the library launches for this head layout and container
+    layout (its dispatch rule: K and V decoded in separate waves for V alphabets
+    of up to 8 levels; a single-wave kernel otherwise)."""
     G = w.n_q_heads // w.n_kv_heads
     if levels_v > 8:
         return f"attention2_kernel<{G}, {w.n_kv_heads}>"
-    return f"attention5_kernel<{G}, {w.n_kv_heads}>"
+    return f"attention5_kernel<{G}, {w.n_kv_heads}, {'true' if tiles else 'false'}>"
 
 
 def run_config(torch, kvq, synth, w, bi, args, dev, extras=False, cpu_sample=False):
@@ -208,7 +208,7 @@ def run_config(torch, kvq, synth, w, bi, args, dev, extras=False, cpu_sample=Fal
         "step_ms": round(ms, 4), "gb_per_s": round(step_bytes / (ms * 1e-3) / 1e9, 2),
         "decode_tokens_per_s": round(w.batch / (ms * 1e-3), 1),
         "kv_token_layers_per_s": round(S * T / (ms * 1e-3), 1),
-        "kernel": kernel_name(w), "kernel_ms": round(kernel_ms, 4),
+        "kernel": kernel_name(w, tiles=args.layout == "tiles"), "kernel_ms": round(kernel_ms, 4),
         "kernel_bytes": kernel_bytes, "kernel_gb_per_s": round(kgbs, 2),
         "kernel_frac_of_hbm_peak": round(kgbs / HBM_PEAK_GBS, 4),
         "kernel_alu_tops": round(alu, 3), "kernel_frac_of_alu_peak": round(alu / VALU_PEAK_TOPS, 4),
