@@ -1011,7 +1011,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-#pragma unroll 1
+#pragma unroll
           for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
             for (int bh = 0; bh < 2; ++bh) {
