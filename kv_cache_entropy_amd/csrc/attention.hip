@@ -224,23 +224,18 @@ __device__ inline float wave_sum_scatter(float (&v)[N], int lane) {
 }
 
 // ------------------------------------------------------------------ prologue
-// One wave per (sequence, KV head, query slot v, chunk of 64 key-mean
-// windows): slot v < G is query head g G + v; slots up to the next multiple
-// of 4 are zero padding.  The chunk-0 wave writes the MFMA A operand (rotated
-// query scaled by 2^e so that max |q| is in [2^7, 2^8), split into fp16
-// hi + lo), the inverse scale and sum_j q_rot_j; every wave writes
-// sum_j q_rot_j mu_w,j for the windows w of its chunk, one per lane.
-__global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
-  const int lane = threadIdx.x;
+// The query terms of one query slot v of KV head g: slot v < G is query head
+// g G + v; slots up to the next multiple of 4 are zero padding.  The chunk-0
+// wave writes the MFMA A operand (rotated query scaled by 2^e so that max |q|
+// is in [2^7, 2^8), split into fp16 hi + lo), the inverse scale and
+// sum_j q_rot_j.  Returns the rotated query (lane holds j = 2 lane, 2 lane + 1).
+__device__ inline void prologue_query(const Prologue2Args& a, int64_t s, int g, int v, int64_t chunk, int lane,
+                                      float (&q)[2]) {
   const int hkv = a.Hq / a.G;
   const int ngm = (a.G + 3) / 4;
-  const int v = int(blockIdx.x % unsigned(ngm * 4));           // query slot in [0, NGM*4)
-  const int64_t chunk = blockIdx.x / unsigned(ngm * 4);        // windows [64 chunk, 64 chunk + 64)
-  const int g = blockIdx.y;
-  const int64_t s = blockIdx.z;
   const bool real = v < a.G;
   const int h = g * a.G + v;
-  float q[2] = {0.f, 0.f};
+  q[0] = q[1] = 0.f;
   if (real) {
     const uint16_t* qp = a.q + (s * a.Hq + h) * kD + lane * 2;
     q[0] = bf16_bits_to_f32(qp[0]);
@@ -274,30 +269,86 @@ __global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
     a.qsum[s * a.Hq + h] = qs;
     a.qscale[s * a.Hq + h] = ldexpf(1.0f, -e);
   }
-  // sum_j q_rot_j mu_w,j: one window per lane, so that the windows' loads are
-  // independent (a long context has thousands of windows per head, spread
-  // over chunks); each lane reads its window's 128 int8 means as 16-byte
-  // vectors (rows are 16-byte aligned: the base is, and n is a multiple of 128).
+}
+
+// sum_j q_rot_j mu_w,j of NH query heads for window w (its 128 int8 means of
+// KV head g, read as 16-byte vectors: rows are 16-byte aligned, since the base
+// is and n is a multiple of 128).  mu_w,j = RN(mu_q sc) is formed once and
+// shared by the heads; each head's sum runs in j order.
+template <int NH>
+__device__ inline void prologue_qmu(const Prologue2Args& a, int64_t s, int g, int64_t w, const float* qsh,
+                                    float (&acc)[NH]) {
+  const float sc = h2f(a.mean_scale[s * a.nW_cap + w]);
+  const uint4* mq = reinterpret_cast<const uint4*>(a.mean_q + (s * a.nW_cap + w) * a.n + int64_t(g) * kD);
+#pragma unroll
+  for (int v = 0; v < NH; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint4 v4 = mq[c];
+    const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float mu = __fmul_rn(float(int8_t(wd[k / 4] >> (8 * (k % 4)))), sc);
+#pragma unroll
+      for (int v = 0; v < NH; ++v) acc[v] = __fadd_rn(acc[v], __fmul_rn(qsh[v * kD + 16 * c + k], mu));
+    }
+  }
+}
+
+// One wave per (sequence, KV head, query slot v, chunk of 64 key-mean
+// windows): the query terms of slot v, and sum_j q_rot_j mu_w,j for the
+// windows w of the chunk, one per lane (a long context has thousands of
+// windows per head, spread over chunks, so the windows' loads are
+// independent).
+__global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
+  const int lane = threadIdx.x;
+  const int ngm = (a.G + 3) / 4;
+  const int v = int(blockIdx.x % unsigned(ngm * 4));           // query slot in [0, NGM*4)
+  const int64_t chunk = blockIdx.x / unsigned(ngm * 4);        // windows [64 chunk, 64 chunk + 64)
+  const int g = blockIdx.y;
+  const int64_t s = blockIdx.z;
+  float q[2];
+  prologue_query(a, s, g, v, chunk, lane, q);
+  if (v >= a.G) return;
   __shared__ float qsh[kD];
   qsh[2 * lane] = q[0];
   qsh[2 * lane + 1] = q[1];
   __syncthreads();
   const int64_t w = chunk * 64 + lane;
   if (w < a.nW) {
-    const float sc = h2f(a.mean_scale[s * a.nW_cap + w]);
-    const uint4* mq = reinterpret_cast<const uint4*>(a.mean_q + (s * a.nW_cap + w) * a.n + int64_t(g) * kD);
-    float acc = 0.f;
+    float acc[1];
+    prologue_qmu<1>(a, s, g, w, qsh, acc);
+    a.qmu[(s * a.Hq + g * a.G + v) * a.nW + w] = acc[0];
+  }
+}
+
+// The same terms with one wave per (sequence, KV head, chunk of 64 windows)
+// for all G <= 4 query heads of the KV head, so that each window's means are
+// loaded and scaled once rather than once per head (launches with enough
+// such waves to fill the GPU).  Every value equals prologue2_kernel's.
+template <int G>
+__global__ __launch_bounds__(64) void prologue_heads_kernel(Prologue2Args a) {
+  const int lane = threadIdx.x;
+  const int64_t chunk = blockIdx.x;
+  const int g = blockIdx.y;
+  const int64_t s = blockIdx.z;
+  __shared__ float qsh[G * kD];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 v4 = mq[c];
-      const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float mu = __fmul_rn(float(int8_t(wd[k / 4] >> (8 * (k % 4)))), sc);
-        acc = __fadd_rn(acc, __fmul_rn(qsh[16 * c + k], mu));
-      }
+  for (int v = 0; v < 4; ++v) {
+    float q[2];
+    prologue_query(a, s, g, v, chunk, lane, q);
+    if (v < G) {
+      qsh[v * kD + 2 * lane] = q[0];
+      qsh[v * kD + 2 * lane + 1] = q[1];
     }
-    a.qmu[(s * a.Hq + h) * a.nW + w] = acc;
+  }
+  __syncthreads();
+  const int64_t w = chunk * 64 + lane;
+  if (w < a.nW) {
+    float acc[G];
+    prologue_qmu<G>(a, s, g, w, qsh, acc);
+#pragma unroll
+    for (int v = 0; v < G; ++v) a.qmu[(s * a.Hq + g * G + v) * a.nW + w] = acc[v];
   }
 }
 
@@ -1551,9 +1602,19 @@ __global__ __launch_bounds__(64) void attention_fw_kernel(Attn2Args a) {
 
 hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t stream) {
   const int ngm = (a.G + 3) / 4;
+  const int hkv = a.Hq / a.G;
   const int64_t chunks = (a.nW + 63) / 64;
   if (chunks * ngm * 4 > int64_t(0x7FFFFFFF)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prologue2_kernel, dim3(unsigned(chunks * ngm * 4), a.Hq / a.G, unsigned(S)), dim3(64), 0,
+  // one wave for all of a KV head's query heads when that still gives at least
+  // 4 waves per CU; else one wave per query slot (more, shorter waves)
+  if (a.G <= 4 && S * hkv * chunks >= 1024) {
+    const dim3 grid{unsigned(chunks), unsigned(hkv), unsigned(S)};
+    if (a.G == 1) hipLaunchKernelGGL(prologue_heads_kernel<1>, grid, dim3(64), 0, stream, a);
+    else if (a.G == 2) hipLaunchKernelGGL(prologue_heads_kernel<2>, grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(prologue_heads_kernel<4>, grid, dim3(64), 0, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(prologue2_kernel, dim3(unsigned(chunks * ngm * 4), unsigned(hkv), unsigned(S)), dim3(64), 0,
                      stream, a);
   return hipGetLastError();
 }
