@@ -614,26 +614,28 @@ __device__ inline uint4 load_chunk_tiles(__amdgpu_buffer_rsrc_t rs, uint32_t off
                     __builtin_amdgcn_raw_buffer_load_b32(rs, off + 768u, 0, 0));
 }
 
+// Positions in a lane's stream are kept in bits (8 per byte), so that the
+// decode step's shift amounts add up to the bytes consumed directly.
 struct Ring5 {
   uint32_t fo;          // buffer offset of the lane's 16-byte aligned frame
   uint32_t off;         // LDS offset of the lane's dword in row 0 of its ring
-  uint32_t P;           // frame position of the next unread byte
-  uint32_t F;           // frame position of the next chunk to fetch
-  uint32_t lim;         // frame position one past the container's last byte
+  uint32_t P;           // frame position of the next unread byte, in bits
+  uint32_t F;           // frame position of the next chunk to fetch, in bits
+  uint32_t lim;         // frame position one past the container's last byte, in bits
   uint4 pend[2];        // chunks in flight
-  uint32_t ppos[2];     // their frame positions (kNoChunk: nothing to write)
+  uint32_t ppos[2];     // their frame positions in bits (kNoChunk: nothing to write)
 };
 
 template <int RS>
 __device__ inline uint32_t ring5_row(uint32_t pos, uint32_t off) {
-  // row (pos / 4) mod 16 at a pitch of 2^RS bytes: one bit-field extract and
+  // row (pos / 32) mod 16 at a pitch of 2^RS bytes: one bit-field extract and
   // one shift-add (opaque keeps the compiler from turning the extract into a
   // shift and a mask)
-  return (opaque(__builtin_amdgcn_ubfe(pos, 2u, 4u)) << RS) + off;
+  return (opaque(__builtin_amdgcn_ubfe(pos, 5u, 4u)) << RS) + off;
 }
 
-// Writes the 16-byte chunk at frame position pos (a multiple of 16, so its
-// four rows do not wrap), and row 16 with it when it lands on row 0.
+// Writes the 16-byte chunk at frame position pos (bits; a multiple of 128, so
+// its four rows do not wrap), and row 16 with it when it lands on row 0.
 template <int RS>
 __device__ inline void ring5_write(uint8_t* lds, uint32_t off, uint32_t pos, const uint4& d) {
   constexpr int R = 1 << (RS - 2);            // dwords per ring row
@@ -642,14 +644,23 @@ __device__ inline void ring5_write(uint8_t* lds, uint32_t off, uint32_t pos, con
   w[R] = d.y;
   w[2 * R] = d.z;
   w[3 * R] = d.w;
-  if ((pos & 63u) == 0u) w[16 * R] = d.x;
+  if ((pos & 511u) == 0u) w[16 * R] = d.x;
 }
 
-// Bytes P .. P+3 of the stream (P's 8-byte window, shifted by P mod 4).
+// Bytes P .. P+3 of the stream as a little-endian dword (P's 8-byte window,
+// shifted by P mod 4 bytes).
 template <int RS>
 __device__ inline uint32_t ring5_window(const Ring5& r, const uint8_t* lds) {
   const uint32_t* w = reinterpret_cast<const uint32_t*>(lds + ring5_row<RS>(r.P, r.off));
-  return __builtin_amdgcn_alignbyte(w[1 << (RS - 2)], w[0], r.P);
+  return __builtin_amdgcn_alignbit(w[1 << (RS - 2)], w[0], r.P);
+}
+
+// The same bytes big-endian: byte P in bits 24..31, as the decode step
+// shifts them into the state from the top.
+template <int RS>
+__device__ inline uint32_t ring5_window_be(const Ring5& r, const uint8_t* lds) {
+  const uint32_t le = ring5_window<RS>(r, lds);
+  return __builtin_amdgcn_perm(le, le, 0x00010203u);
 }
 
 // Starts a container (cont_off: its byte offset in the sequence's buffer
@@ -661,19 +672,19 @@ __device__ inline uint32_t ring5_start(Ring5& r, uint8_t* lds, __amdgpu_buffer_r
                                        uint32_t C) {
   const uint32_t off0 = TL ? 0u : cont_off & 15u;
   r.fo = cont_off - off0;
-  r.lim = off0 + C;
+  r.lim = 8u * (off0 + C);
   uint4 d[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    d[q] = TL ? load_chunk_tiles(rs, uint32_t(16 * q) < r.lim ? r.fo + 1024u * q : kNoLoad)
-              : load_chunk(rs, uint32_t(16 * q) < r.lim ? r.fo + 16u * q : kNoLoad);
+    d[q] = TL ? load_chunk_tiles(rs, 128u * q < r.lim ? r.fo + 1024u * q : kNoLoad)
+              : load_chunk(rs, 128u * q < r.lim ? r.fo + 16u * q : kNoLoad);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ring5_write<RS>(lds, r.off, 16u * q, d[q]);
-  r.F = 64u;
+  for (int q = 0; q < 4; ++q) ring5_write<RS>(lds, r.off, 128u * q, d[q]);
+  r.F = 512u;
   r.ppos[0] = r.ppos[1] = kNoChunk;
-  r.P = off0;
+  r.P = 8u * off0;
   const uint32_t x = ring5_window<RS>(r, lds);
-  r.P = off0 + 4u;
+  r.P += 32u;
   return x;
 }
 
@@ -685,37 +696,48 @@ __device__ inline uint32_t ring5_start(Ring5& r, uint8_t* lds, __amdgpu_buffer_r
 template <int S, int RS, bool TL = false>
 __device__ inline void ring5_block(Ring5& r, uint8_t* lds, __amdgpu_buffer_rsrc_t rs) {
   if (r.ppos[S] != kNoChunk) ring5_write<RS>(lds, r.off, r.ppos[S], r.pend[S]);
-  const bool real = (r.F < r.lim) && (r.F - r.P <= 48u);
-  r.pend[S] = TL ? load_chunk_tiles(rs, real ? r.fo + 64u * r.F : kNoLoad) : load_chunk(rs, real ? r.fo + r.F : kNoLoad);
+  const bool real = (r.F < r.lim) && (r.F - r.P <= 384u);
+  r.pend[S] = TL ? load_chunk_tiles(rs, real ? r.fo + 8u * r.F : kNoLoad)
+                 : load_chunk(rs, real ? r.fo + (r.F >> 3) : kNoLoad);
   r.ppos[S] = real ? r.F : kNoChunk;
-  r.F += real ? 16u : 0u;
+  r.F += real ? 128u : 0u;
 }
 
-// Selector of v_perm that yields (x << 8) | byte j of the window (j = low byte).
-constexpr uint32_t kSel0 = 0x06050400u;
-
 // One symbol of Algorithm 2: x = f (x >> 8) + z - c, then at most one byte
-// shifted in.  win holds the next 4 stream bytes and sel counts those already
-// taken in the current group of 4 symbols, so the update is branch-free and
-// reads no LDS besides the table.  Returns the table entry.
+// shifted in.  xw holds the state in its high half and the next stream bytes,
+// big-endian, in its low half, so the byte shift-in is one 64-bit shift by 8
+// or 0 bits that also moves the window on; the shift amount (bits consumed)
+// is returned in sh.  Reads no LDS besides the table; returns the table entry.
 // PERM: the table slot is row x mod 256 of the interleaved table region at
 // TAB, so the address is one v_perm: byte 0 from the lane's replica offset
 // toff, byte 1 the state's low byte, bytes 2..3 zero; TAB is an immediate.
 // Otherwise slot z holds its replicas contiguously (toff = table base + the
 // lane's replica offset) and the address is a shift and an and-or.
 template <bool PERM, uint32_t SLOT_SHIFT, uint32_t TAB>
-__device__ inline uint32_t dec5_step(uint32_t& x, uint32_t win, uint32_t& sel, const uint8_t* lds, uint32_t toff) {
+__device__ inline uint32_t dec5_step(uint64_t& xw, uint32_t& sh, const uint8_t* lds, uint32_t toff) {
   constexpr uint32_t mask = 0xFFu << SLOT_SHIFT;
+  const uint32_t x = uint32_t(xw >> 32);
   const uint32_t addr = PERM ? __builtin_amdgcn_perm(x, toff, 0x0C0C0400u) + TAB
                              : (((x << SLOT_SHIFT) & mask) | toff);
   const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + addr);
   const uint32_t m = opaque(__umul24(e & 0xFFu, x >> 8));
-  x = m + ((e >> 8) & 0xFFu);
-  const bool renorm = x < kStateLow;
-  const uint32_t xs = __builtin_amdgcn_perm(x, win, sel);
-  x = renorm ? xs : x;
-  sel = opaque(sel + (renorm ? 1u : 0u));
+  const uint32_t x1 = m + ((e >> 8) & 0xFFu);
+  // opaque: a shift by a selected amount, not a select between two shifts
+  sh = opaque(x1 < kStateLow ? 8u : 0u);
+  xw = ((uint64_t(x1) << 32) | uint32_t(xw)) << sh;
   return e;
+}
+
+// Four symbols from the window at the lane's position; advances the position
+// by the bits they consumed.
+template <bool PERM, uint32_t SLOT_SHIFT, uint32_t TAB, int RS>
+__device__ inline void dec5_group(uint32_t& x, Ring5& r, const uint8_t* lds, uint32_t toff, uint32_t (&e)[4]) {
+  uint64_t xw = (uint64_t(x) << 32) | ring5_window_be<RS>(r, lds);
+  uint32_t sh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = dec5_step<PERM, SLOT_SHIFT, TAB>(xw, sh[i], lds, toff);
+  x = uint32_t(xw >> 32);
+  r.P = r.P + sh[0] + sh[1] + sh[2] + sh[3];
 }
 
 // 4x4x4 MFMA whose A operand is broadcast from block `abid` to all 16 blocks.
@@ -1071,11 +1093,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
 #pragma unroll
               for (int cc = 0; cc < 4; ++cc) {
                 uint32_t e[4];
-                const uint32_t winK = ring5_window<RS>(rk, lds);
-                uint32_t selk = kSel0;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) e[r] = dec5_step<PERM, Lay::SLOT_SHIFT, TAB>(xk, winK, selk, lds, toffK);
-                rk.P += selk - kSel0;
+                dec5_group<PERM, Lay::SLOT_SHIFT, TAB, RS>(xk, rk, lds, toffK, e);
                 const half4_t B = as_half4(__builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
                                            __builtin_amdgcn_perm(e[3], e[2], 0x07060302u));
 #pragma unroll
@@ -1213,14 +1231,10 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
               else ring5_block<0, RS, TL>(rv, lds, rsV);
 #pragma unroll
               for (int cc = 0; cc < 4; ++cc) {
-                const uint32_t winV = ring5_window<RS>(rv, lds);
-                uint32_t selv = kSel0;
+                uint32_t ev[4];
+                dec5_group<PERM, Lay::SLOT_SHIFT, TAB, RS>(xv, rv, lds, toffV, ev);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  const uint32_t ev = dec5_step<PERM, Lay::SLOT_SHIFT, TAB>(xv, winV, selv, lds, toffV);
-                  vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
-                }
-                rv.P += selv - kSel0;
+                for (int r = 0; r < 4; ++r) vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev[r] >> 16);
               }
             }
           if (ch == 0) pair_wait(ready, step + 1u);     // the K wave's weights of (i, g)
@@ -1288,14 +1302,10 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
             else ring5_block<0, RS, TL>(rv, lds, rsV);
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
-              const uint32_t winV = ring5_window<RS>(rv, lds);
-              uint32_t selv = kSel0;
+              uint32_t ev[4];
+              dec5_group<PERM, Lay::SLOT_SHIFT, TAB, RS>(xv, rv, lds, toffV, ev);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const uint32_t ev = dec5_step<PERM, Lay::SLOT_SHIFT, TAB>(xv, winV, selv, lds, toffV);
-                vc[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev >> 16);
-              }
-              rv.P += selv - kSel0;
+              for (int r = 0; r < 4; ++r) vc[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev[r] >> 16);
             }
           }
         if (two_vch) {
