@@ -865,16 +865,17 @@ struct Lay5 {
 // every pair to the slowest one at each step).  The K wave posts `ready` =
 // j + 1 once the weights of its step j are in LDS; the V wave posts `done` =
 // j + 1 once it has read them.  Only LDS accesses are ordered around the
-// counters: container loads in flight stay in flight.  The wait is bounded
-// (about 2^20 sleeps of 64 clocks, far beyond any step) so that no wave can
-// spin for ever; both waves of a pair run the same step sequence, so the
-// bound is never reached in a correct run.
+// counters: container loads in flight stay in flight.  A waiting wave polls
+// once per 256-clock sleep, so that its polls take little issue time from the
+// waves that share its SIMD.  The wait is bounded (2^20 polls, far beyond any
+// step) so that no wave can spin for ever; both waves of a pair run the same
+// step sequence, so the bound is never reached in a correct run.
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 __device__ __forceinline__ void pair_wait(const uint32_t* counter, uint32_t want) {
   for (uint32_t it = 0; it < kSpinLimit; ++it) {
     if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= want) break;
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(4);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
