@@ -86,14 +86,19 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineA
   const int per = (cnt + nwv - 1) / nwv;
   const int kb = wv * per;
   const int ke = kb + per < cnt ? kb + per : cnt;
+  // with one round of splits (the common case) the maximum comes from that
+  // round's own loads; otherwise from a pass over the splits' maxima first
+  const bool one_round = ke - kb <= kCombineChunk;
   float Mx = -__builtin_inff();
-  for (int k = kb + lane; k < ke; k += 64) Mx = fmaxf(Mx, P[int64_t(k) * step * sp + a.d]);
-  Mx = wave_max(Mx);
+  if (!one_round) {
+    for (int k = kb + lane; k < ke; k += 64) Mx = fmaxf(Mx, P[int64_t(k) * step * sp + a.d]);
+    Mx = wave_max(Mx);
+  }
   float L = 0.f, Z = 0.f;
   float acc[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) acc[i] = 0.f;
-  if (Mx > -__builtin_inff()) {
+  if (one_round || Mx > -__builtin_inff()) {
     for (int k0 = kb; k0 < ke; k0 += kCombineChunk) {
       const int kn = ke - k0 < kCombineChunk ? ke - k0 : kCombineChunk;
       // every load of the round first: lane j < kn the max and sums of split
@@ -111,6 +116,10 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineA
 #pragma unroll
         for (int i = 0; i < NPL; ++i)
           v[j][i] = j < kn ? P[int64_t(k0 + j) * step * sp + lane * NPL + i] : 0.f;
+      if (one_round) {
+        Mx = wave_max(mk);
+        if (!(Mx > -__builtin_inff())) break;           // no split holds a token
+      }
       const float sck = lane < kn ? __expf(mk - Mx) : 0.f;
       L += wave_sum_f32(sck * lk);
       Z += wave_sum_f32(sck * zk);
