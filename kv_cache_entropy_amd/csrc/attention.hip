@@ -228,9 +228,10 @@ __device__ inline float wave_sum_scatter(float (&v)[N], int lane) {
 // g G + v; slots up to the next multiple of 4 are zero padding.  The chunk-0
 // wave writes the MFMA A operand (rotated query scaled by 2^e so that max |q|
 // is in [2^7, 2^8), split into fp16 hi + lo), the inverse scale and
-// sum_j q_rot_j.  Returns the rotated query (lane holds j = 2 lane, 2 lane + 1).
+// sum_j q_rot_j.  Returns the rotated query (lane holds j = 2 lane, 2 lane + 1)
+// and its scale 2^e in up_out.
 __device__ inline void prologue_query(const Prologue2Args& a, int64_t s, int g, int v, int64_t chunk, int lane,
-                                      float (&q)[2]) {
+                                      float (&q)[2], float* up_out = nullptr) {
   const int hkv = a.Hq / a.G;
   const int ngm = (a.G + 3) / 4;
   const bool real = v < a.G;
@@ -250,6 +251,7 @@ __device__ inline void prologue_query(const Prologue2Args& a, int64_t s, int g, 
     e = 8 - ex;
   }
   const float up = ldexpf(1.0f, e);
+  if (up_out) *up_out = up;
   // operand layout: [s][g][gm][c = j/4][n][hi0..3 lo0..3]
   const int gm = v / 4, n = v % 4;
   uint16_t* op = a.qop + ((((s * hkv + g) * ngm + gm) * 32) * 4) * 8;
@@ -319,36 +321,6 @@ __global__ __launch_bounds__(64) void prologue2_kernel(Prologue2Args a) {
     float acc[1];
     prologue_qmu<1>(a, s, g, w, qsh, acc);
     a.qmu[(s * a.Hq + g * a.G + v) * a.nW + w] = acc[0];
-  }
-}
-
-// The same terms with one wave per (sequence, KV head, chunk of 64 windows)
-// for all G <= 4 query heads of the KV head, so that each window's means are
-// loaded and scaled once rather than once per head (launches with enough
-// such waves to fill the GPU).  Every value equals prologue2_kernel's.
-template <int G>
-__global__ __launch_bounds__(64) void prologue_heads_kernel(Prologue2Args a) {
-  const int lane = threadIdx.x;
-  const int64_t chunk = blockIdx.x;
-  const int g = blockIdx.y;
-  const int64_t s = blockIdx.z;
-  __shared__ float qsh[G * kD];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    float q[2];
-    prologue_query(a, s, g, v, chunk, lane, q);
-    if (v < G) {
-      qsh[v * kD + 2 * lane] = q[0];
-      qsh[v * kD + 2 * lane + 1] = q[1];
-    }
-  }
-  __syncthreads();
-  const int64_t w = chunk * 64 + lane;
-  if (w < a.nW) {
-    float acc[G];
-    prologue_qmu<G>(a, s, g, w, qsh, acc);
-#pragma unroll
-    for (int v = 0; v < G; ++v) a.qmu[(s * a.Hq + g * G + v) * a.nW + w] = acc[v];
   }
 }
 
@@ -757,6 +729,87 @@ __device__ __attribute__((always_inline)) inline float4_t mfma_bcast_a(half4_t a
       return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, 15, 0);
   }
 #undef KVQ_MFMA_BCAST_CASE
+}
+
+// The query terms with one wave per (sequence, KV head, chunk of 64 key-mean
+// windows) for all G <= 4 query heads of the KV head: sum_j q_rot_j mu_w,j
+// for the chunk's windows is a [4 heads x 128] x [128 x 64 windows] product
+// on 4x4x4 MFMA blocks.  Lane 4 b + n holds window 64 chunk + 4 b + n: its
+// 128 int8 means are the B operand (4 per k-step, exact in fp16); the A
+// operand, the rotated query scaled by 2^e and split into fp16 hi + lo, is
+// broadcast from the block that holds the k-step (set t, block b: k-step
+// 16 t + b, lane 4 b + m: head slot m).  The products are exact in fp32 and
+// accumulate in fp32; the sum is then scaled by the window's mean scale and
+// 2^-e.  Slots v >= G are zero.
+template <int G>
+__global__ __launch_bounds__(64) void prologue_mfma_kernel(Prologue2Args a) {
+  const int lane = threadIdx.x;
+  const int64_t chunk = blockIdx.x;
+  const int g = blockIdx.y;
+  const int64_t s = blockIdx.z;
+  __shared__ float qsh[4][kD];
+  __shared__ float upsh[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float q[2], up;
+    prologue_query(a, s, g, v, chunk, lane, q, &up);
+    qsh[v][2 * lane] = q[0];
+    qsh[v][2 * lane + 1] = q[1];
+    if (lane == 0) upsh[v] = up;
+  }
+  __syncthreads();
+  // A operand sets: lane 4 b + m, k-step c = 16 t + b of head slot m
+  const int m = lane & 3, b = lane >> 2;
+  const float upm = upsh[m];
+  uint32_t ahi[2][2], alo[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float4 qv = *reinterpret_cast<const float4*>(&qsh[m][4 * (16 * t + b)]);
+    const float qs[4] = {qv.x * upm, qv.y * upm, qv.z * upm, qv.w * upm};   // exact: a power of two
+    uint32_t hb[4], lb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const __half hi = __float2half_rn(qs[k]);
+      hb[k] = __half_as_ushort(hi);
+      lb[k] = __half_as_ushort(__float2half_rn(qs[k] - __half2float(hi)));
+    }
+    ahi[t][0] = hb[0] | (hb[1] << 16);
+    ahi[t][1] = hb[2] | (hb[3] << 16);
+    alo[t][0] = lb[0] | (lb[1] << 16);
+    alo[t][1] = lb[2] | (lb[3] << 16);
+  }
+  // B operand: the lane's window (zero past the windows attended)
+  const int64_t w = chunk * 64 + lane;
+  uint4 mv[8];
+  float sc = 0.f;
+  if (w < a.nW) {
+    sc = h2f(a.mean_scale[s * a.nW_cap + w]);
+    const uint4* mq = reinterpret_cast<const uint4*>(a.mean_q + (s * a.nW_cap + w) * a.n + int64_t(g) * kD);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) mv[c] = mq[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) mv[c] = uint4{0u, 0u, 0u, 0u};
+  }
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const half2v off = {_Float16(1152.0f), _Float16(1152.0f)};
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    const uint32_t d = c % 4 == 0 ? mv[c / 4].x : c % 4 == 1 ? mv[c / 4].y : c % 4 == 2 ? mv[c / 4].z : mv[c / 4].w;
+    // int8 x -> fp16: the bits 0x6400 | (x + 128) are 1024 + x + 128; minus 1152
+    const uint32_t u = d ^ 0x80808080u;
+    const half2v lo = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off;
+    const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off;
+    const half4_t B = {lo.x, lo.y, hi.x, hi.y};
+    acc = mfma_bcast_a(as_half4(ahi[c / 16][0], ahi[c / 16][1]), B, acc, c % 16);
+    acc = mfma_bcast_a(as_half4(alo[c / 16][0], alo[c / 16][1]), B, acc, c % 16);
+  }
+  if (w < a.nW) {
+#pragma unroll
+    for (int v = 0; v < G; ++v)
+      a.qmu[(s * a.Hq + g * G + v) * a.nW + w] = acc[v] * (sc / upsh[v]);
+  }
 }
 
 // PV over the 64 tokens of a tile for 64 channels: the int8 level indices of
@@ -1616,13 +1669,14 @@ hipError_t launch_prologue2(const Prologue2Args& a, int64_t S, hipStream_t strea
   const int hkv = a.Hq / a.G;
   const int64_t chunks = (a.nW + 63) / 64;
   if (chunks * ngm * 4 > int64_t(0x7FFFFFFF)) return hipErrorInvalidValue;
-  // one wave for all of a KV head's query heads when that still gives at least
-  // 4 waves per CU; else one wave per query slot (more, shorter waves)
+  // up to 4 query heads per KV head and at least 4 such waves per CU: one wave
+  // for all of them, the window sums on MFMA; otherwise one wave per query
+  // slot (more, shorter waves)
   if (a.G <= 4 && S * hkv * chunks >= 1024) {
     const dim3 grid{unsigned(chunks), unsigned(hkv), unsigned(S)};
-    if (a.G == 1) hipLaunchKernelGGL(prologue_heads_kernel<1>, grid, dim3(64), 0, stream, a);
-    else if (a.G == 2) hipLaunchKernelGGL(prologue_heads_kernel<2>, grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL(prologue_heads_kernel<4>, grid, dim3(64), 0, stream, a);
+    if (a.G == 1) hipLaunchKernelGGL(prologue_mfma_kernel<1>, grid, dim3(64), 0, stream, a);
+    else if (a.G == 2) hipLaunchKernelGGL(prologue_mfma_kernel<2>, grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(prologue_mfma_kernel<4>, grid, dim3(64), 0, stream, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(prologue2_kernel, dim3(unsigned(chunks * ngm * 4), unsigned(hkv), unsigned(S)), dim3(64), 0,
