@@ -226,6 +226,107 @@ __device__ bool drift(const float (&x)[NPL], float s, float o, const EncShared& 
   return false;
 }
 
+// drift for an alphabet of exactly MC levels: the same result, with the argmin
+// of each value taken as the minimum of its MC objectives (three-operand
+// minimums) and then the lowest level whose objective equals it - the level a
+// scan with strict < keeps - in fewer instructions than the scan.
+template <int NPL, int MC>
+__device__ bool drift_exact(const float (&x)[NPL], float s, float o, const EncShared& sh,
+                      int levels, uint8_t (&m)[NPL], uint8_t (*near)[NPL]) {
+  // distortions, their range over all (i, level), and the nearest levels
+  float dmax = 0.f, dmin = __builtin_inff();
+  float Dc[MC][NPL];
+  float bestD[NPL];
+  uint32_t bl[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) { bestD[i] = __builtin_inff(); bl[i] = 0; }
+  (void)levels;                         // == MC
+#pragma unroll
+  for (int l = 0; l < MC; ++l) {
+    const float rec = __fadd_rn(o, __fmul_rn(s, sh.level[l]));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const float dl = __fsub_rn(x[i], rec);
+      const float D = __fmul_rn(dl, dl);
+      Dc[l][i] = D;
+      dmax = fmaxf(dmax, D);
+      dmin = fminf(dmin, D);
+      const bool lt = D < bestD[i];
+      bestD[i] = lt ? D : bestD[i];
+      bl[i] = lt ? uint32_t(l) : bl[i];
+    }
+  }
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) (*near)[i] = uint8_t(bl[i]);
+  }
+  dmax = wave_ext_dpp<true>(dmax);
+  dmin = wave_ext_dpp<false>(dmin);
+  const float y = __fmul_rn(__fsub_rn(dmax, dmin), 8.0f);
+  const uint8_t cheap = uint8_t(sh.cheapest);
+  if (!(y > 0.f)) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) m[i] = cheap;
+    return false;
+  }
+  int e;
+  const float fr = frexpf(y, &e);
+  const int hi0 = (fr == 0.5f) ? e - 1 : e;
+  int lo = 512 * (hi0 - 40), hi = 512 * hi0;
+  bool moved = false;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) m[i] = cheap;
+  uint32_t cur[NPL];
+  for (int step = 0; step <= 12; ++step) {
+    int u;
+    if (step < 12) {
+      u = (lo + hi) >> 1;              // lo + hi is always even: exact
+    } else {
+      if (moved) break;
+      u = hi;                          // never feasible inside: try 2^hi
+    }
+    const float lam = ldexpf(sh.lambda[u & 511], u >> 9);
+    float lr[MC];
+#pragma unroll
+    for (int l = 0; l < MC; ++l) lr[l] = __fmul_rn(lam, sh.rate_f[l]);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      float obj[MC];
+#pragma unroll
+      for (int l = 0; l < MC; ++l) obj[l] = __fadd_rn(Dc[l][i], lr[l]);
+      // sums, never signalling NaNs: the minimums need no canonicalisation;
+      // a NaN objective never equals the minimum, as it never beats one
+      float best = obj[0];
+#pragma unroll
+      for (int l = 1; l < MC; ++l) best = __builtin_fminf(best, obj[l]);
+      uint32_t c = 0;
+#pragma unroll
+      for (int l = MC - 1; l >= 0; --l) c = obj[l] == best ? uint32_t(l) : c;
+      cur[i] = c;
+    }
+    uint32_t R = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) R += sh.rate_fx[cur[i]];
+    R = wave_sum_u32_dpp(R);
+    const bool ok = uint64_t(R) <= sh.budget_fx;
+    if (step < 12) {
+      if (ok) {
+        hi = u;
+        moved = true;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) m[i] = uint8_t(cur[i]);
+      } else {
+        lo = u;
+      }
+    } else {
+      if (!ok) return true;            // fallback: cheapest level everywhere
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) m[i] = uint8_t(cur[i]);
+    }
+  }
+  return false;
+}
+
 // The same without the cache, for alphabets above MC levels.
 template <int NPL>
 __device__ bool drift_large(const float (&x)[NPL], float s, float o, const EncShared& sh,
@@ -447,7 +548,9 @@ __device__ bool rans_encode_lane(const uint8_t* sym, int n, uint8_t* img, int C,
 // streams of up to 16 values per lane: 128 registers).
 constexpr int kDriftCache = 8;
 
-template <int NPL, int FWB>
+// ML > 0: the alphabet has exactly ML levels (the cached drift in its exact
+// form); 0: any alphabet.
+template <int NPL, int FWB, int ML = 0>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
   constexpr bool FW = FWB != 0;
   extern __shared__ __align__(16) uint8_t dyn[];
@@ -504,7 +607,11 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
       if constexpr (FW) fw_pack_lane<NPL, FWB>(m, reinterpret_cast<uint32_t*>(img + size_t(sl) * CS), lane);
     } else {
       uint8_t near[NPL];
-      if (NPL * kDriftCache <= 128 && M <= kDriftCache) {
+      if constexpr (ML > 0) {
+        fb1 += drift_exact<NPL, ML>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
+        refit<NPL>(x, m, s, o, n, sh.level, s16, o16);
+        fb2 += drift_exact<NPL, ML>(x, __half2float(s16), __half2float(o16), sh, M, m, &near) ? 1u : 0u;
+      } else if (NPL * kDriftCache <= 128 && M <= kDriftCache) {
         constexpr int MC = NPL * kDriftCache <= 128 ? kDriftCache : 1;
         fb1 += drift<NPL, MC>(x, s, o, sh, M, m, nullptr) ? 1u : 0u;
         refit<NPL>(x, m, s, o, n, sh.level, s16, o16);
@@ -599,6 +706,26 @@ hipError_t launch_encode(const EncodeArgs& a, int64_t n_streams, hipStream_t str
       case 64 * 16 + 2: hipLaunchKernelGGL((encode_kernel<64, 2>), grid, block, lds, stream, a); break;
       case 64 * 16 + 4: hipLaunchKernelGGL((encode_kernel<64, 4>), grid, block, lds, stream, a); break;
       case 64 * 16 + 8: hipLaunchKernelGGL((encode_kernel<64, 8>), grid, block, lds, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  // the exact-size drift for the 8- and 6-level alphabets (their objectives
+  // fit the registers up to 16 values per lane)
+  const int L = a.tabs.levels;
+  if ((L == 8 || L == 6) && a.n / 64 <= 16) {
+    const int key = (a.n / 64) * 16 + L;
+    switch (key) {
+      case 1 * 16 + 8: hipLaunchKernelGGL((encode_kernel<1, 0, 8>), grid, block, lds, stream, a); break;
+      case 1 * 16 + 6: hipLaunchKernelGGL((encode_kernel<1, 0, 6>), grid, block, lds, stream, a); break;
+      case 2 * 16 + 8: hipLaunchKernelGGL((encode_kernel<2, 0, 8>), grid, block, lds, stream, a); break;
+      case 2 * 16 + 6: hipLaunchKernelGGL((encode_kernel<2, 0, 6>), grid, block, lds, stream, a); break;
+      case 4 * 16 + 8: hipLaunchKernelGGL((encode_kernel<4, 0, 8>), grid, block, lds, stream, a); break;
+      case 4 * 16 + 6: hipLaunchKernelGGL((encode_kernel<4, 0, 6>), grid, block, lds, stream, a); break;
+      case 8 * 16 + 8: hipLaunchKernelGGL((encode_kernel<8, 0, 8>), grid, block, lds, stream, a); break;
+      case 8 * 16 + 6: hipLaunchKernelGGL((encode_kernel<8, 0, 6>), grid, block, lds, stream, a); break;
+      case 16 * 16 + 8: hipLaunchKernelGGL((encode_kernel<16, 0, 8>), grid, block, lds, stream, a); break;
+      case 16 * 16 + 6: hipLaunchKernelGGL((encode_kernel<16, 0, 6>), grid, block, lds, stream, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
