@@ -938,6 +938,23 @@ __device__ __forceinline__ void pair_post(uint32_t* counter, uint32_t value, int
   if (lane == 0) __hip_atomic_store(counter, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// In a full workgroup the waves of pairs p and p ^ 4 share a SIMD (wave w
+// runs on SIMD w mod 4).  Issue favours the older waves, so without a
+// correction pairs 0..3 run ahead and finish well before pairs 4..7, which
+// then finish the launch with half the waves on each SIMD.  Once per step
+// each wave compares its pair's progress with the other pair's (the same
+// counter kind: ready for K waves, done for V waves) and takes the higher
+// issue priority while its pair is behind, so the two pairs finish together.
+// This changes only the order of issue, never what is computed.
+__device__ __forceinline__ void balance_issue(uint32_t mine, const uint32_t* other) {
+  const uint32_t theirs =
+      __builtin_amdgcn_readfirstlane(__hip_atomic_load(other, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+  if (mine < theirs)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // pv_half for integer V levels (every fp16 level has a zero low byte): the
 // chunk holds the levels' fp16 high bytes (the V table entries carry them in
 // place of the level index), and two v_perms place them over zero low bytes.
@@ -1042,6 +1059,12 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
   float* const alv = reinterpret_cast<float*>(lds + Lay::alv_off(pw));
   uint32_t* const ready = reinterpret_cast<uint32_t*>(lds + Lay::alv_off(pw) + Lay::READY);
   uint32_t* const done = reinterpret_cast<uint32_t*>(lds + Lay::alv_off(pw) + Lay::DONE);
+  // the other pair on this wave's SIMD (full workgroups only)
+  const bool balance = np == kPairs;
+  const uint32_t* const other_ready =
+      reinterpret_cast<const uint32_t*>(lds + Lay::alv_off(pw ^ (kPairs / 2)) + Lay::READY);
+  const uint32_t* const other_done =
+      reinterpret_cast<const uint32_t*>(lds + Lay::alv_off(pw ^ (kPairs / 2)) + Lay::DONE);
   uint32_t step = 0;                  // steps of this wave so far (tile i, KV head g)
   float* const runM = reinterpret_cast<float*>(PERM ? lds + Lay::piece(4 * pw) : mine + Lay::RUN);
   float* const runL = PERM ? reinterpret_cast<float*>(lds + Lay::piece(4 * pw + 1)) : runM + HQ;
@@ -1096,6 +1119,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
       const int64_t tK = tb + 64 * i;
 #pragma unroll 1
       for (int g = 0; g < HKV; ++g) {
+        if (balance) balance_issue(step, other_ready);
         if (g == 0) {
           const int64_t row = s * a.T_cap + tK + lane;
           xk = ring5_start<RS, TL>(
@@ -1263,6 +1287,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
       const int64_t tV = tb + 64 * i;
 #pragma unroll 1
       for (int g = 0; g < HKV; ++g) {
+        if (balance) balance_issue(step, other_done);
         if (g == 0) xv = ring5_start<RS, TL>(rv, lds, rsV,
                                              TL ? misV + uint32_t(tV) * uint32_t(a.CVs) + uint32_t(lane) * 4u
                                                 : misV + uint32_t(tV + lane) * uint32_t(a.CV),
@@ -1320,6 +1345,7 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
     const int64_t tV = tb + 64 * i;
 #pragma unroll 1
     for (int g = 0; g < HKV; ++g) {
+      if (balance) balance_issue(step, other_done);
       if (g == 0) xv = ring5_start<RS, TL>(rv, lds, rsV,
                                              TL ? misV + uint32_t(tV) * uint32_t(a.CVs) + uint32_t(lane) * 4u
                                                 : misV + uint32_t(tV + lane) * uint32_t(a.CV),
