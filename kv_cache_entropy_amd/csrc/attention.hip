@@ -712,6 +712,27 @@ __device__ inline void dec5_group(uint32_t& x, Ring5& r, const uint8_t* lds, uin
   r.P = r.P + sh[0] + sh[1] + sh[2] + sh[3];
 }
 
+// dec5_group for the V wave: each symbol's level byte goes to its row of the
+// level chunk, one symbol late, so that every byte store follows the next
+// symbol's table read (LDS instructions of a wave run in order; a store
+// queued ahead of a read would lengthen the decode chain).  row0 is the
+// address of the group's first symbol in its row; epend carries the pending
+// entry (skipped before the first symbol of a run, flushed by the caller).
+template <bool PERM, uint32_t SLOT_SHIFT, uint32_t TAB, int RS>
+__device__ inline void dec5_group_v(uint32_t& x, Ring5& r, const uint8_t* lds, uint32_t toff, uint8_t* row0,
+                                    uint32_t& epend, bool first) {
+  uint64_t xw = (uint64_t(x) << 32) | ring5_window_be<RS>(r, lds);
+  uint32_t sh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t e = dec5_step<PERM, SLOT_SHIFT, TAB>(xw, sh[i], lds, toff);
+    if (!(first && i == 0)) row0[(i - 1) * kChunk8Stride] = uint8_t(epend >> 16);
+    epend = e;
+  }
+  x = uint32_t(xw >> 32);
+  r.P = r.P + sh[0] + sh[1] + sh[2] + sh[3];
+}
+
 // 4x4x4 MFMA whose A operand is broadcast from block `abid` to all 16 blocks.
 // The builtin needs the block as a literal; callers pass a value that is a
 // constant after unrolling, so the switch folds to one instruction.
@@ -1302,20 +1323,21 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll 1
-          for (int b2 = 0; b2 < 2; ++b2)
+          for (int b2 = 0; b2 < 2; ++b2) {
+            uint32_t epend = 0;
 #pragma unroll
             for (int bh = 0; bh < 2; ++bh) {
               const int b4 = 2 * b2 + bh;
               if (bh == 1) ring5_block<1, RS, TL>(rv, lds, rsV);
               else ring5_block<0, RS, TL>(rv, lds, rsV);
 #pragma unroll
-              for (int cc = 0; cc < 4; ++cc) {
-                uint32_t ev[4];
-                dec5_group<PERM, Lay::SLOT_SHIFT, TAB, RS>(xv, rv, lds, toffV, ev);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) vch[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev[r] >> 16);
-              }
+              for (int cc = 0; cc < 4; ++cc)
+                dec5_group_v<PERM, Lay::SLOT_SHIFT, TAB, RS>(xv, rv, lds, toffV,
+                                                             vch + (b4 * 16 + cc * 4) * kChunk8Stride + lane, epend,
+                                                             bh == 0 && cc == 0);
             }
+            vch[(b2 * 32 + 31) * kChunk8Stride + lane] = uint8_t(epend >> 16);
+          }
           if (ch == 0) pair_wait(ready, step + 1u);     // the K wave's weights of (i, g)
           wave_lds_fence();
           if (lo_levels)
@@ -1374,20 +1396,21 @@ __global__ __launch_bounds__(128 * kPairs, 1) void attention5_kernel(Attn2Args a
       for (int ch = 0; ch < 2; ++ch) {
         uint8_t* const vc = vch + (ch == 1 && two_vch ? kVch2 : 0u);
 #pragma unroll 1
-        for (int b2 = 0; b2 < 2; ++b2)
+        for (int b2 = 0; b2 < 2; ++b2) {
+          uint32_t epend = 0;
 #pragma unroll
           for (int bh = 0; bh < 2; ++bh) {
             const int b4 = 2 * b2 + bh;
             if (bh == 1) ring5_block<1, RS, TL>(rv, lds, rsV);
             else ring5_block<0, RS, TL>(rv, lds, rsV);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-              uint32_t ev[4];
-              dec5_group<PERM, Lay::SLOT_SHIFT, TAB, RS>(xv, rv, lds, toffV, ev);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) vc[(b4 * 16 + cc * 4 + r) * kChunk8Stride + lane] = uint8_t(ev[r] >> 16);
-            }
+            for (int cc = 0; cc < 4; ++cc)
+              dec5_group_v<PERM, Lay::SLOT_SHIFT, TAB, RS>(xv, rv, lds, toffV,
+                                                           vc + (b4 * 16 + cc * 4) * kChunk8Stride + lane, epend,
+                                                           bh == 0 && cc == 0);
           }
+          vc[(b2 * 32 + 31) * kChunk8Stride + lane] = uint8_t(epend >> 16);
+        }
         if (two_vch) {
           // both halves decoded before the step's weights are needed
           if (ch == 1) {
