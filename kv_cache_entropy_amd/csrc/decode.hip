@@ -184,6 +184,65 @@ __global__ __launch_bounds__(64 * kCombineMaxWaves) void combine_kernel(CombineA
   }
 }
 
+// Few splits (at most kCombineChunk): one wave per (query head, sequence)
+// merges all of them in one round, kCombineHeads heads per workgroup and no
+// LDS, so that the launch's many small workgroups are not held back by the
+// multi-wave kernel's reduction buffer (8 KiB per workgroup) and run in
+// fewer rounds.  Same arithmetic as one wave of combine_kernel in one round.
+constexpr int kCombineHeads = 8;
+
+template <int NPL>
+__global__ __launch_bounds__(64 * kCombineHeads) void combine_heads_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int h = int(blockIdx.x) * kCombineHeads + int(threadIdx.x >> 6);
+  if (h >= a.Hq) return;
+  const int64_t s = blockIdx.y;
+  const int stride = a.d + 4;
+  const int64_t sp = int64_t(a.Hq) * stride;
+  const int kn = a.nsplit;                            // <= kCombineChunk
+  const float* P = a.part + s * a.nsplit * sp + int64_t(h) * stride;
+  float mk = -__builtin_inff(), lk = 0.f, zk = 0.f;
+  if (lane < kn) {
+    const float* Pk = P + int64_t(lane) * sp;
+    mk = Pk[a.d];
+    lk = Pk[a.d + 1];
+    zk = Pk[a.d + 2];
+  }
+  float v[kCombineChunk][NPL];
+#pragma unroll
+  for (int j = 0; j < kCombineChunk; ++j)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) v[j][i] = j < kn ? P[int64_t(j) * sp + lane * NPL + i] : 0.f;
+  const float M = wave_max(mk);
+  float acc[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) acc[i] = 0.f;
+  float L = 0.f, Z = 0.f;
+  if (M > -__builtin_inff()) {
+    const float sck = lane < kn ? __expf(mk - M) : 0.f;
+    L = wave_sum_f32(sck * lk);
+    Z = wave_sum_f32(sck * zk);
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j) {
+      const float sc = __shfl(sck, j, 64);            // 0 past kn
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) acc[i] += sc * v[j][i];
+    }
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) acc[i] = (acc[i] + Z) * inv;
+  fwht_lanes<NPL>(acc, a.d, lane, a.hscale);
+  const int64_t ob = (s * a.Hq + h) * a.d + lane * NPL;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const uint32_t u = __float_as_uint(acc[i]);
+    const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    a.out[ob + i] = uint16_t(r >> 16);
+    if (a.out_f32) a.out_f32[ob + i] = acc[i];
+  }
+}
+
 // ---------------------------------------------------------------- residual
 // The most recent tokens of every sequence kept uncompressed in bf16
 // ([D-Quant] §5.1 "Implementation details") join the same softmax as one more
@@ -308,6 +367,11 @@ hipError_t launch_decode_symbols(const DecSymArgs& a, hipStream_t stream) {
 
 template <int NPL>
 static hipError_t launch_combine_t(const CombineArgs& a, int64_t S, hipStream_t stream) {
+  if (a.nsplit <= kCombineChunk) {
+    const dim3 grid(unsigned((a.Hq + kCombineHeads - 1) / kCombineHeads), unsigned(S));
+    hipLaunchKernelGGL((combine_heads_kernel<NPL>), grid, dim3(64 * kCombineHeads), 0, stream, a);
+    return hipGetLastError();
+  }
   int group = 1;
   if (a.nsplit > kCombineTwoPass) {
     group = kCombineGroup;
