@@ -247,12 +247,46 @@ __global__ __launch_bounds__(64 * kCombineHeads) void combine_heads_kernel(Combi
 // The most recent tokens of every sequence kept uncompressed in bf16
 // ([D-Quant] §5.1 "Implementation details") join the same softmax as one more
 // split of partials.  One wave per (KV head, sequence): per 64-token chunk,
-// lane t computes the logits of token t for the G query heads, the chunk's
+// lane t gets the logits of token t for the G query heads, the chunk's
 // max / sum update the running softmax state, and lane j then accumulates
 // channels 2j, 2j+1 of sum_t p_t v_t.  The accumulator is rotated (orthonormal
 // Hadamard, its own inverse) so that it matches the rotated partials of the
 // compressed splits; the offset sum Z is zero.
+//
+// The logits are a [4 heads x 128] x [128 x 64 tokens] product per group of 4
+// query heads on bf16 4x4x4 MFMA blocks: block b, column n is token 4 b + n
+// (the lane's own token), whose key row supplies the B operand 4 channels per
+// k-step straight from its bf16 pairs; the query is the A operand, broadcast
+// from the block that holds the k-step (k-step c in block c mod 16, slot
+// c / 16).  Products of bf16 values are exact in fp32 and accumulate in fp32.
+// The result of block b is the lane's 4 heads' logits.
 constexpr int kResMaxG = 8;
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float res_f4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4_t as_bf16x4(uint32_t lo, uint32_t hi) {
+  const uint2 u = {lo, hi};
+  return __builtin_bit_cast(bf16x4_t, u);
+}
+
+// bf16 4x4x4 MFMA with the A operand broadcast from block `abid` (a literal
+// after unrolling, so the switch folds to one instruction).
+__device__ __attribute__((always_inline)) inline res_f4_t mfma_bf16_bcast(bf16x4_t a, bf16x4_t b, res_f4_t c,
+                                                                          int abid) {
+#define KVQ_RES_MFMA_CASE(i) \
+  case i:                    \
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 4, i, 0);
+  switch (abid) {
+    KVQ_RES_MFMA_CASE(0) KVQ_RES_MFMA_CASE(1) KVQ_RES_MFMA_CASE(2) KVQ_RES_MFMA_CASE(3)
+    KVQ_RES_MFMA_CASE(4) KVQ_RES_MFMA_CASE(5) KVQ_RES_MFMA_CASE(6) KVQ_RES_MFMA_CASE(7)
+    KVQ_RES_MFMA_CASE(8) KVQ_RES_MFMA_CASE(9) KVQ_RES_MFMA_CASE(10) KVQ_RES_MFMA_CASE(11)
+    KVQ_RES_MFMA_CASE(12) KVQ_RES_MFMA_CASE(13) KVQ_RES_MFMA_CASE(14)
+    default:
+      return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 4, 15, 0);
+  }
+#undef KVQ_RES_MFMA_CASE
+}
 
 __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
   const int lane = threadIdx.x;
@@ -260,13 +294,17 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
   const int64_t s = blockIdx.y;
   const int G = a.G, d = a.d;                 // d == 128: two channels per lane
   const int hkv = a.Hq / G;
-  __shared__ float qs[kResMaxG][128];
   __shared__ float ps[kResMaxG][64];
-  for (int i = lane; i < G * d; i += 64) {
-    const int h = i / d, j = i % d;
-    qs[h][j] = bf16_bits_to_f32(a.q[(s * a.Hq + g * G + h) * d + j]);
-  }
-  __syncthreads();
+  // A operands: query head 4 m + (lane & 3), channels 4 c .. 4 c + 3 of
+  // k-steps c = lane / 4 and lane / 4 + 16 (zero for head slots >= G)
+  uint2 qa[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int h = 4 * m + (lane & 3), c = (lane >> 2) + 16 * i;
+      qa[m][i] = h < G ? *reinterpret_cast<const uint2*>(a.q + (s * a.Hq + g * G + h) * d + 4 * c) : uint2{0u, 0u};
+    }
   float M[kResMaxG], L[kResMaxG], acc[kResMaxG][2];
 #pragma unroll
   for (int h = 0; h < kResMaxG; ++h) {
@@ -280,28 +318,27 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
   for (int64_t t0 = 0; t0 < a.R; t0 += 64) {
     const int64_t t = t0 + lane;
     const bool live = t < a.R;
-    float lg[kResMaxG];
-#pragma unroll
-    for (int h = 0; h < kResMaxG; ++h) lg[h] = 0.f;
+    // the token's 128 key values as 16 independent 16-byte loads (zero past the tail)
+    uint4 kv[16];
     if (live) {
-      // the token's 128 key values as 16 independent 16-byte loads
       const uint4* kr = reinterpret_cast<const uint4*>(kb + t * row_stride);
-      uint4 kv[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) kv[c] = kr[c];
+    } else {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const uint32_t w4[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 8 * c + 2 * e;
-          const float k0 = __uint_as_float(w4[e] << 16), k1 = __uint_as_float(w4[e] & 0xFFFF0000u);
-#pragma unroll
-          for (int h = 0; h < kResMaxG; ++h)
-            if (h < G) lg[h] += qs[h][j] * k0 + qs[h][j + 1] * k1;
-        }
-      }
+      for (int c = 0; c < 16; ++c) kv[c] = uint4{0u, 0u, 0u, 0u};
     }
+    res_f4_t D[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const bf16x4_t B = (c & 1) ? as_bf16x4(kv[c >> 1].z, kv[c >> 1].w) : as_bf16x4(kv[c >> 1].x, kv[c >> 1].y);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        if (4 * m < G) D[m] = mfma_bf16_bcast(as_bf16x4(qa[m][c >> 4].x, qa[m][c >> 4].y), B, D[m], c & 15);
+    }
+    float lg[kResMaxG];
+#pragma unroll
+    for (int h = 0; h < kResMaxG; ++h) lg[h] = D[h >> 2][h & 3];
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < kResMaxG; ++h) {

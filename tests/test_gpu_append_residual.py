@@ -121,3 +121,40 @@ def test_attention_with_residual(appended, n_tok, res_len):
     say(f"  max row-normwise error {err:.3e}")
     assert err <= TOL
     assert torch.equal(out32.cpu().to(torch.bfloat16).view(torch.int16), out.cpu().view(torch.int16))
+
+
+@pytest.mark.parametrize("hkv,hq,res_len", [(8, 8, 70), (4, 8, 129), (8, 64, 100), (2, 16, 1), (1, 4, 64)])
+def test_residual_only_head_layouts(hkv, hq, res_len):
+    """A bf16 tail with no compressed prefix, for 1, 2, 4 and 8 query heads per
+    KV head: the tail kernel's logits, softmax and value sums against the
+    oracle's float64 attention over the raw tail."""
+    from kv_cache_entropy_amd import kvq
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    d, S, RCAP = 128, 3, 160
+    n = hkv * d
+    say(f"case residual only: Hkv={hkv} Hq={hq} tail {res_len}")
+    g = torch.Generator().manual_seed(1000 * hkv + hq + res_len)
+    q = (torch.randn(S, hq, d, generator=g) * 0.5).to(torch.bfloat16)
+    rk = torch.zeros(S, RCAP, n, dtype=torch.bfloat16)
+    rv = torch.zeros(S, RCAP, n, dtype=torch.bfloat16)
+    rk[:, :res_len] = (torch.randn(S, res_len, n, generator=g) * 0.7).to(torch.bfloat16)
+    rv[:, :res_len] = torch.randn(S, res_len, n, generator=g).to(torch.bfloat16)
+    ck = max(36, (n * 9) // 32)
+    cv = max(36, (n * 7) // 32)
+    plan = kvq.Plan(hkv, d, 8, 6, ck, cv, 128, 1.4)
+    ws = torch.empty(plan.workspace_bytes(1, S, 0, hq), dtype=torch.uint8, device="cuda")
+    out = torch.empty(S, hq, d, dtype=torch.bfloat16, device="cuda")
+    out32 = torch.empty(S, hq, d, dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_attention_ex(plan, q.cuda(), None, 0, rk.cuda(), rv.cuda(), res_len, out, ws, out_f32=out32)
+    torch.cuda.synchronize()
+    empty = np.zeros((0, n))
+    err = 0.0
+    for i in range(S):
+        ref = O.attention_with_residual_f64(q[i].float().numpy(), empty, empty, rk[i, :res_len].float().numpy(),
+                                            rv[i, :res_len].float().numpy(), hkv, d)
+        o32 = out32[i].cpu().numpy().astype(np.float64)
+        err = max(err, (np.abs(o32 - ref).max(axis=-1) / np.abs(ref).max(axis=-1)).max())
+    say(f"  max row-normwise error {err:.3e}")
+    assert err <= TOL
+    assert torch.equal(out32.cpu().to(torch.bfloat16).view(torch.int16), out.cpu().view(torch.int16))
