@@ -295,6 +295,10 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
   const int G = a.G, d = a.d;                 // d == 128: two channels per lane
   const int hkv = a.Hq / G;
   __shared__ float ps[kResMaxG][64];
+  // the chunk's value rows, token t at t * kResRow bytes (16 bytes of padding
+  // per row spread the lanes' 16-byte stores over the banks)
+  constexpr int kResRow = 272;
+  __shared__ __align__(16) uint8_t vst[64 * kResRow];
   // A operands: query head 4 m + (lane & 3), channels 4 c .. 4 c + 3 of
   // k-steps c = lane / 4 and lane / 4 + 16 (zero for head slots >= G)
   uint2 qa[2][2];
@@ -339,6 +343,18 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
     float lg[kResMaxG];
 #pragma unroll
     for (int h = 0; h < kResMaxG; ++h) lg[h] = D[h >> 2][h & 3];
+    // the token's value row, loaded like its key row (in flight during the
+    // softmax) and staged in LDS, so that the products below read value rows
+    // from LDS instead of waiting on memory 8 rows at a time
+    uint4 vv[16];
+    if (live) {
+      const uint4* vr = reinterpret_cast<const uint4*>(vb + t * row_stride);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) vv[c] = vr[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) vv[c] = uint4{0u, 0u, 0u, 0u};
+    }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < kResMaxG; ++h) {
@@ -354,15 +370,14 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
         ps[h][lane] = p;
       }
     }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) *reinterpret_cast<uint4*>(vst + lane * kResRow + 16 * c) = vv[c];
     __syncthreads();
     const int tn = int(a.R - t0 < 64 ? a.R - t0 : 64);
     for (int u0 = 0; u0 < tn; u0 += 8) {
-      // 8 value rows in flight (rows past the tail are not loaded)
       uint32_t two[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        two[e] = u0 + e < tn ? *reinterpret_cast<const uint32_t*>(vb + (t0 + u0 + e) * row_stride + 2 * lane)
-                             : 0u;
+      for (int e = 0; e < 8; ++e) two[e] = *reinterpret_cast<const uint32_t*>(vst + (u0 + e) * kResRow + 4 * lane);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v0 = __uint_as_float(two[e] << 16), v1 = __uint_as_float(two[e] & 0xFFFF0000u);
