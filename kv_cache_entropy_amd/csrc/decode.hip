@@ -295,10 +295,11 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
   const int G = a.G, d = a.d;                 // d == 128: two channels per lane
   const int hkv = a.Hq / G;
   __shared__ float ps[kResMaxG][64];
-  // the chunk's value rows, token t at t * kResRow bytes (16 bytes of padding
-  // per row spread the lanes' 16-byte stores over the banks)
+  // half a chunk's value rows, token t at (t mod 32) kResRow bytes (16 bytes
+  // of padding per row spread the lanes' 16-byte stores over the banks); half
+  // a chunk keeps the workgroup's LDS small enough for 12 waves per CU
   constexpr int kResRow = 272;
-  __shared__ __align__(16) uint8_t vst[64 * kResRow];
+  __shared__ __align__(16) uint8_t vst[32 * kResRow];
   // A operands: query head 4 m + (lane & 3), channels 4 c .. 4 c + 3 of
   // k-steps c = lane / 4 and lane / 4 + 16 (zero for head slots >= G)
   uint2 qa[2][2];
@@ -370,26 +371,32 @@ __global__ __launch_bounds__(64) void residual_kernel(ResidualArgs a) {
         ps[h][lane] = p;
       }
     }
-#pragma unroll
-    for (int c = 0; c < 16; ++c) *reinterpret_cast<uint4*>(vst + lane * kResRow + 16 * c) = vv[c];
-    __syncthreads();
     const int tn = int(a.R - t0 < 64 ? a.R - t0 : 64);
-    for (int u0 = 0; u0 < tn; u0 += 8) {
-      uint32_t two[8];
+    for (int hb = 0; hb < tn; hb += 32) {
+      if ((lane >> 5) == (hb >> 5)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) two[e] = *reinterpret_cast<const uint32_t*>(vst + (u0 + e) * kResRow + 4 * lane);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v0 = __uint_as_float(two[e] << 16), v1 = __uint_as_float(two[e] & 0xFFFF0000u);
-#pragma unroll
-        for (int h = 0; h < kResMaxG; ++h)
-          if (h < G && u0 + e < tn) {
-            acc[h][0] += ps[h][u0 + e] * v0;
-            acc[h][1] += ps[h][u0 + e] * v1;
-          }
+        for (int c = 0; c < 16; ++c) *reinterpret_cast<uint4*>(vst + (lane & 31) * kResRow + 16 * c) = vv[c];
       }
+      __syncthreads();
+      const int he = tn < hb + 32 ? tn : hb + 32;
+      for (int u0 = hb; u0 < he; u0 += 8) {
+        uint32_t two[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          two[e] = *reinterpret_cast<const uint32_t*>(vst + ((u0 + e) & 31) * kResRow + 4 * lane);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v0 = __uint_as_float(two[e] << 16), v1 = __uint_as_float(two[e] & 0xFFFF0000u);
+#pragma unroll
+          for (int h = 0; h < kResMaxG; ++h)
+            if (h < G && u0 + e < he) {
+              acc[h][0] += ps[h][u0 + e] * v0;
+              acc[h][1] += ps[h][u0 + e] * v1;
+            }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
   const int stride = d + 4;
 #pragma unroll
